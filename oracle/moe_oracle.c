@@ -1,0 +1,364 @@
+/*
+ * CPU ORACLE for the Grok-1 mixture-of-experts feed-forward layer.
+ *
+ * Test infrastructure only: the parity tests, the smoke check and the bench's
+ * CPU-baseline leg call it. The GPU library never links, loads or calls it,
+ * and it shares no code, header or table with the GPU library.
+ *
+ * Plain and slow on purpose: every result is accumulated in double precision
+ * in the order the definition reads, one token and one expert at a time, with
+ * no blocking, fusion or reordering. Threads only split independent tokens or
+ * (token, expert) assignments.
+ *
+ * What the layer computes (Grok-1 field guide, "MoE 子层" section; Grok-1
+ * book ch. 10 "与其他 MoE 对比", section 10.3.1, the Grok-1 routing code;
+ * section 10.4, the GeGLU box):
+ *   1. router: logit[t][e] = sum_i x[t][i] * Wr[e][i]           (no bias)
+ *   2. p[t] = softmax(logit[t]) over all E experts
+ *   3. the k largest p (ties: lower expert index first) are the selected
+ *      experts; their gates are those p values, NOT renormalised
+ *   4. expert e (gated FFN, no biases):
+ *        a[j] = sum_i x[i] Wg[e][j][i],  b[j] = sum_i x[i] Wu[e][j][i]
+ *        h[j] = GELU(a[j]) * b[j],  GELU(z) = z * Phi(z) = z (1 + erf(z/sqrt2)) / 2
+ *        y[i] = sum_j h[j] Wd[e][i][j]
+ *   5. out[t] = sum over selected slots s (in slot order) of gate[t][s] * y_s
+ * Plus the expert-contiguous permutation the sparse dispatch needs (book ch.
+ * 11, section 11.3.1: sparse reorder + grouped GEMM instead of running all
+ * experts densely).
+ *
+ * Storage layouts: x [T][d]; Wr [E][d]; Wg, Wu [E][f][d]; Wd [E][d][f].
+ * Element types: ORC_F64, ORC_F32, ORC_BF16 (uint16 bit patterns) and
+ * ORC_I8 (int8 values q; the weight is q * scale with one fp32 scale per
+ * output channel, packed [gate: E*f | up: E*f | down: E*d]).
+ *
+ * Readings where the pages are silent (also listed in the design notes):
+ * exact-erf GELU on the gate branch; fp64 logits; ties to the lower index;
+ * gates in slot order with slot 0 the larger; segment rows in ascending token
+ * order.
+ *
+ * Parity pins: every function here is checked by the CPU test suite against
+ * closed forms, invariants, brute force or independent library routines.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F64 = 0, ORC_F32 = 1, ORC_BF16 = 2, ORC_I8 = 3 };
+
+#define ORC_OK 0
+#define ORC_EINVAL (-1)
+#define ORC_ENOMEM (-2)
+
+static double elem(const void* p, int dt, int64_t i) {
+  switch (dt) {
+    case ORC_F64: return ((const double*)p)[i];
+    case ORC_F32: return (double)((const float*)p)[i];
+    case ORC_BF16: {
+      uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
+      float f;
+      memcpy(&f, &u, 4);
+      return (double)f;
+    }
+    case ORC_I8: return (double)((const int8_t*)p)[i];
+  }
+  return NAN;
+}
+
+static int valid_dt(int dt) { return dt >= ORC_F64 && dt <= ORC_I8; }
+
+static int set_threads(int nthreads) {
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_num_procs();
+  return nthreads;
+#else
+  (void)nthreads;
+  return 1;
+#endif
+}
+
+/* GELU with the exact Gaussian CDF: z * Phi(z), Phi(z) = (1 + erf(z / sqrt 2)) / 2
+ * (book ch. 10, section 10.4, GeGLU vs SwiGLU box). */
+double oracle_gelu(double z) { return 0.5 * z * (1.0 + erf(z / sqrt(2.0))); }
+
+/* Steps 1-3 for one token: logits, softmax over all experts, top-k without
+ * renormalisation (book ch. 10, section 10.3.1, the Grok-1 code). */
+static void route_token(const void* x, int xdt, const void* wr, int rdt, int64_t t, int64_t d, int E,
+                        int k, double* p, int32_t* idx, double* gate) {
+  double logit[64];
+  for (int e = 0; e < E; ++e) {
+    double s = 0.0;
+    for (int64_t i = 0; i < d; ++i) s += elem(x, xdt, t * d + i) * elem(wr, rdt, (int64_t)e * d + i);
+    logit[e] = s;
+  }
+  double mx = logit[0];
+  for (int e = 1; e < E; ++e)
+    if (logit[e] > mx) mx = logit[e];
+  double z = 0.0;
+  for (int e = 0; e < E; ++e) z += exp(logit[e] - mx);
+  for (int e = 0; e < E; ++e) p[e] = exp(logit[e] - mx) / z;
+  /* selection by the key (-p, e): largest probability first, lower index on ties */
+  int taken[64] = {0};
+  for (int s = 0; s < k; ++s) {
+    int best = -1;
+    for (int e = 0; e < E; ++e) {
+      if (taken[e]) continue;
+      if (best < 0 || p[e] > p[best]) best = e;
+    }
+    taken[best] = 1;
+    idx[s] = best;
+    gate[s] = p[best];
+  }
+}
+
+/* probs [T][E] (nullable), idx [T][k], gate [T][k]. */
+int oracle_route(const void* x, int xdt, const void* router_w, int rdt, int64_t T, int64_t d, int E, int k,
+                 double* probs, int32_t* idx, double* gate, int nthreads) {
+  if (T < 0 || d < 1 || E < 1 || E > 64 || k < 1 || k > E || !valid_dt(xdt) || !valid_dt(rdt)) return ORC_EINVAL;
+  if (T > 0 && (!x || !router_w || !idx || !gate)) return ORC_EINVAL;
+  int nt = set_threads(nthreads);
+  (void)nt;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+  for (int64_t t = 0; t < T; ++t) {
+    double p[64];
+    route_token(x, xdt, router_w, rdt, t, d, E, k, p, idx + t * k, gate + t * k);
+    if (probs)
+      for (int e = 0; e < E; ++e) probs[t * E + e] = p[e];
+  }
+  return ORC_OK;
+}
+
+/* Expert-contiguous permutation of the k*T assignments (sparse reorder, book
+ * ch. 11, section 11.3.1). counts[e] = #assignments to e; offsets = exclusive
+ * scan (E+1 entries); segment e lists its tokens in ascending token order;
+ * perm[row] = token; pos[t][s] = the row of assignment (t, s). */
+int oracle_permute(const int32_t* idx, int64_t T, int E, int k, int32_t* counts, int32_t* offsets,
+                   int32_t* perm, int32_t* pos) {
+  if (T < 0 || E < 1 || k < 1 || k > E || !counts || !offsets) return ORC_EINVAL;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t a = 0; a < T * k; ++a) {
+    int e = idx[a];
+    if (e < 0 || e >= E) return ORC_EINVAL;
+    counts[e] += 1;
+  }
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  if (!fill) return ORC_ENOMEM;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int s = 0; s < k; ++s) {
+      int e = idx[t * k + s];
+      int32_t row = offsets[e] + fill[e];
+      fill[e] += 1;
+      perm[row] = (int32_t)t;
+      pos[t * k + s] = row;
+    }
+  }
+  free(fill);
+  return ORC_OK;
+}
+
+/* Weight element readers with the per-output-channel scale of 8-bit weights. */
+typedef struct {
+  const void *wg, *wu, *wd;
+  int wdt;
+  const float* scales;
+  int64_t d, f;
+  int E;
+} weights_t;
+
+static double w_gate(const weights_t* w, int e, int64_t j, int64_t i) {
+  double v = elem(w->wg, w->wdt, ((int64_t)e * w->f + j) * w->d + i);
+  if (w->wdt == ORC_I8) v *= (double)w->scales[(int64_t)e * w->f + j];
+  return v;
+}
+static double w_up(const weights_t* w, int e, int64_t j, int64_t i) {
+  double v = elem(w->wu, w->wdt, ((int64_t)e * w->f + j) * w->d + i);
+  if (w->wdt == ORC_I8) v *= (double)w->scales[(int64_t)w->E * w->f + (int64_t)e * w->f + j];
+  return v;
+}
+static double w_down(const weights_t* w, int e, int64_t i, int64_t j) {
+  double v = elem(w->wd, w->wdt, ((int64_t)e * w->d + i) * w->f + j);
+  if (w->wdt == ORC_I8) v *= (double)w->scales[2 * (int64_t)w->E * w->f + (int64_t)e * w->d + i];
+  return v;
+}
+
+/* Step 4: token row x (d values) through expert e; y gets d values; h (f values) is scratch. */
+static void expert_ffn(const weights_t* w, const double* x, int e, double* h, double* y) {
+  const int64_t d = w->d, f = w->f;
+  for (int64_t j = 0; j < f; ++j) {
+    double a = 0.0, b = 0.0;
+    for (int64_t i = 0; i < d; ++i) {
+      a += x[i] * w_gate(w, e, j, i);
+      b += x[i] * w_up(w, e, j, i);
+    }
+    h[j] = oracle_gelu(a) * b;
+  }
+  for (int64_t i = 0; i < d; ++i) {
+    double s = 0.0;
+    for (int64_t j = 0; j < f; ++j) s += h[j] * w_down(w, e, i, j);
+    y[i] = s;
+  }
+}
+
+static int check_weights(int wdt, const float* scales) {
+  if (!valid_dt(wdt)) return 0;
+  if (wdt == ORC_I8 && !scales) return 0;
+  return 1;
+}
+
+/* Single expert output for one token (used by tests for per-expert checks). */
+int oracle_expert(const void* x, int xdt, int64_t t, const void* wg, const void* wu, const void* wd, int wdt,
+                  const float* scales, int64_t d, int64_t f, int E, int e, double* y) {
+  if (!check_weights(wdt, scales) || !valid_dt(xdt) || e < 0 || e >= E || d < 1 || f < 1) return ORC_EINVAL;
+  weights_t w = {wg, wu, wd, wdt, scales, d, f, E};
+  double* xr = (double*)malloc(sizeof(double) * (size_t)d);
+  double* h = (double*)malloc(sizeof(double) * (size_t)f);
+  if (!xr || !h) { free(xr); free(h); return ORC_ENOMEM; }
+  for (int64_t i = 0; i < d; ++i) xr[i] = elem(x, xdt, t * d + i);
+  expert_ffn(&w, xr, e, h, y);
+  free(xr);
+  free(h);
+  return ORC_OK;
+}
+
+/* Steps 4-5 for a list of tokens, given the routing (idx [T][k], gate [T][k]).
+ * out has ntok rows of d values: row r is token tokens[r] (all T tokens when
+ * tokens is NULL, then ntok must equal T). */
+int oracle_forward_given_routing(const void* x, int xdt, const void* wg, const void* wu, const void* wd, int wdt,
+                                 const float* scales, const int32_t* idx, const double* gate, int64_t T,
+                                 int64_t d, int64_t f, int E, int k, const int64_t* tokens, int64_t ntok,
+                                 double* out, int nthreads) {
+  if (!check_weights(wdt, scales) || !valid_dt(xdt) || T < 0 || d < 1 || f < 1 || E < 1 || k < 1 || k > E)
+    return ORC_EINVAL;
+  if (!tokens && ntok != T) return ORC_EINVAL;
+  if (ntok == 0) return ORC_OK;
+  for (int64_t r = 0; r < ntok; ++r) {
+    int64_t t = tokens ? tokens[r] : r;
+    if (t < 0 || t >= T) return ORC_EINVAL;
+    for (int s = 0; s < k; ++s)
+      if (idx[t * k + s] < 0 || idx[t * k + s] >= E) return ORC_EINVAL;
+  }
+  weights_t w = {wg, wu, wd, wdt, scales, d, f, E};
+  /* y[r][s][:] = output of the expert in slot s for token tokens[r] */
+  double* y = (double*)malloc(sizeof(double) * (size_t)(ntok * k * d));
+  if (!y) return ORC_ENOMEM;
+  int nt = set_threads(nthreads);
+  (void)nt;
+  int fail = 0;
+#pragma omp parallel num_threads(nt)
+  {
+    double* xr = (double*)malloc(sizeof(double) * (size_t)d);
+    double* h = (double*)malloc(sizeof(double) * (size_t)f);
+    if (!xr || !h) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t a = 0; a < ntok * k; ++a) {
+        int64_t r = a / k;
+        int s = (int)(a % k);
+        int64_t t = tokens ? tokens[r] : r;
+        for (int64_t i = 0; i < d; ++i) xr[i] = elem(x, xdt, t * d + i);
+        expert_ffn(&w, xr, idx[t * k + s], h, y + a * d);
+      }
+    }
+    free(xr);
+    free(h);
+  }
+  if (fail) { free(y); return ORC_ENOMEM; }
+  for (int64_t r = 0; r < ntok; ++r) {
+    int64_t t = tokens ? tokens[r] : r;
+    for (int64_t i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (int s = 0; s < k; ++s) acc += gate[t * k + s] * y[(r * k + s) * d + i];
+      out[r * d + i] = acc;
+    }
+  }
+  free(y);
+  return ORC_OK;
+}
+
+/* The whole layer: route every token, then steps 4-5 for every token.
+ * idx/gate (nullable) receive the routing. */
+int oracle_forward(const void* x, int xdt, const void* router_w, int rdt, const void* wg, const void* wu,
+                   const void* wd, int wdt, const float* scales, int64_t T, int64_t d, int64_t f, int E, int k,
+                   double* out, int32_t* idx_out, double* gate_out, int nthreads) {
+  if (T < 0 || E < 1 || E > 64 || k < 1 || k > E) return ORC_EINVAL;
+  if (T == 0) return ORC_OK;
+  int32_t* idx = idx_out ? idx_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * k));
+  double* gate = gate_out ? gate_out : (double*)malloc(sizeof(double) * (size_t)(T * k));
+  int rc = ORC_ENOMEM;
+  if (idx && gate) {
+    rc = oracle_route(x, xdt, router_w, rdt, T, d, E, k, NULL, idx, gate, nthreads);
+    if (rc == ORC_OK)
+      rc = oracle_forward_given_routing(x, xdt, wg, wu, wd, wdt, scales, idx, gate, T, d, f, E, k, NULL, T, out,
+                                        nthreads);
+  }
+  if (!idx_out) free(idx);
+  if (!gate_out) free(gate);
+  return rc;
+}
+
+/* Brute force in the pages' own dense formulation (book ch. 11, section
+ * 11.3.1 and 11.5.2: every expert runs on every token, then a one-hot mask of
+ * the top-k keeps the selected outputs, each times its gate). The expert math
+ * is written out again here, with different loop nesting, so that this path
+ * shares no helper with the sparse one above except the element reader, GELU
+ * and the router. */
+int oracle_dense_onehot(const void* x, int xdt, const void* router_w, int rdt, const void* wg, const void* wu,
+                        const void* wd, int wdt, const float* scales, int64_t T, int64_t d, int64_t f, int E,
+                        int k, double* out, int nthreads) {
+  if (!check_weights(wdt, scales) || !valid_dt(xdt) || T < 0 || d < 1 || f < 1 || E < 1 || E > 64 || k < 1 ||
+      k > E)
+    return ORC_EINVAL;
+  weights_t w = {wg, wu, wd, wdt, scales, d, f, E};
+  int nt = set_threads(nthreads);
+  (void)nt;
+  int fail = 0;
+#pragma omp parallel num_threads(nt)
+  {
+    double* a = (double*)malloc(sizeof(double) * (size_t)f);
+    double* b = (double*)malloc(sizeof(double) * (size_t)f);
+    double* ye = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!a || !b || !ye) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t t = 0; t < T; ++t) {
+        double p[64], g[64], mask[64];
+        int32_t id[64];
+        route_token(x, xdt, router_w, rdt, t, d, E, k, p, id, g);
+        for (int e = 0; e < E; ++e) mask[e] = 0.0;
+        for (int s = 0; s < k; ++s) mask[id[s]] = g[s];
+        for (int64_t i = 0; i < d; ++i) out[t * d + i] = 0.0;
+        for (int e = 0; e < E; ++e) {
+          /* up-projections accumulated input-feature-outer */
+          for (int64_t j = 0; j < f; ++j) a[j] = b[j] = 0.0;
+          for (int64_t i = 0; i < d; ++i) {
+            double xi = elem(x, xdt, t * d + i);
+            for (int64_t j = 0; j < f; ++j) {
+              a[j] += xi * w_gate(&w, e, j, i);
+              b[j] += xi * w_up(&w, e, j, i);
+            }
+          }
+          /* down-projection as a sum of columns h[j] * Wd[:, j] */
+          for (int64_t i = 0; i < d; ++i) ye[i] = 0.0;
+          for (int64_t j = 0; j < f; ++j) {
+            double hj = oracle_gelu(a[j]) * b[j];
+            for (int64_t i = 0; i < d; ++i) ye[i] += hj * w_down(&w, e, i, j);
+          }
+          for (int64_t i = 0; i < d; ++i) out[t * d + i] += mask[e] * ye[i];
+        }
+      }
+    }
+    free(a);
+    free(b);
+    free(ye);
+  }
+  return fail ? ORC_ENOMEM : ORC_OK;
+}
