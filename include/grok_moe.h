@@ -1,0 +1,150 @@
+/*
+ * grok_moe.h - C ABI of the MI355X (gfx950) Grok-1 mixture-of-experts
+ * feed-forward layer.
+ *
+ * The operation (Grok-1 field guide, "MoE 子层" section; Grok-1 book ch. 10,
+ * section 10.3.1 for the routing code and section 10.4 for the GeGLU expert):
+ *
+ *   logits[t][e] = sum_i x[t][i] * router_w[e][i]          (no bias)
+ *   p[t]         = softmax(logits[t]) over all E experts
+ *   (idx, gate)  = the k largest p[t][e], largest first, lower index on
+ *                  exact ties; the gates are those p values, NOT renormalised
+ *   for each selected expert e of token t:
+ *     a[j] = sum_i x[t][i] w_gate[e][j][i],  b[j] = sum_i x[t][i] w_up[e][j][i]
+ *     h[j] = GELU(a[j]) * b[j],  GELU(z) = z * Phi(z)   (exact erf, no tanh)
+ *     y[i] = sum_j h[j] w_down[e][i][j]
+ *   out[t] = sum over the k slots (in slot order) of gate * y
+ *
+ * The experts run sparsely: tokens are permuted into expert-contiguous rows
+ * and each expert runs as one segment of a grouped GEMM (the sparse reorder
+ * plus grouped GEMM that book ch. 11, section 11.3.1 names as what
+ * deployment needs instead of running all experts densely).
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller; the library
+ *    keeps no pointer after the call returns.
+ *  - Layouts are row-major and contiguous:
+ *      x, out    [T][d]
+ *      router_w  [E][d]         row e = the d router weights of expert e
+ *      w_gate    [E][f][d]      row j of expert e = the d input weights of
+ *      w_up      [E][f][d]        its channel j (output-channel-major)
+ *      w_down    [E][d][f]      row i of expert e = the f weights of output i
+ *      scales    fp32, [gate: E*f | up: E*f | down: E*d]; 8-bit weights only;
+ *                the weight is q * scale of its output channel
+ *  - Asynchronous: a return of GROK_MOE_OK means the work is enqueued on
+ *    `stream` (a hipStream_t; NULL is the default stream). Nothing is
+ *    synchronised and nothing is copied to the host; device faults surface at
+ *    the caller's next synchronisation. Buffers must stay valid until the
+ *    stream work completes.
+ *  - Arguments are validated before anything is enqueued: a failing call
+ *    enqueues nothing and writes nothing.
+ *  - `out` must not alias any input. T = 0 is a no-op that returns OK.
+ *  - Supported shapes (GROK_MOE_EUNSUPPORTED otherwise): 1 <= k <= min(E, 8),
+ *    E <= 64, bf16 and 8-bit weights need d % 128 == 0 and f % 256 == 0;
+ *    fp32 needs d % 8 == 0 and f % 4 == 0; T <= 2^20.
+ *  - Pointers must be 16-byte aligned (GROK_MOE_EALIGN otherwise).
+ *  - Thread-safe: no global mutable state. Concurrent calls on different
+ *    streams need separate workspaces (the plain forms allocate their own).
+ */
+#ifndef GROK_MOE_H
+#define GROK_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GROK_MOE_OK = 0,
+  GROK_MOE_EINVAL = -1,        /* null pointer, negative size, k > E, bad dtype */
+  GROK_MOE_EUNSUPPORTED = -2,  /* a shape outside the supported set above */
+  GROK_MOE_EALIGN = -3,        /* a pointer that is not 16-byte aligned */
+  GROK_MOE_EWORKSPACE = -4,    /* workspace smaller than grok_moe_workspace_bytes() */
+  GROK_MOE_EHIP = -5           /* a HIP runtime call (allocation or launch) failed */
+} grok_moe_status;
+
+/* element types */
+enum { GROK_MOE_BF16 = 0, GROK_MOE_F32 = 1, GROK_MOE_I8 = 2 };
+
+/* Full argument set of one layer call. act_dtype is the type of x, router_w
+ * and out (GROK_MOE_BF16 or GROK_MOE_F32); w_dtype the type of the expert
+ * weights (GROK_MOE_BF16 with bf16 activations, GROK_MOE_I8 with bf16
+ * activations and `scales`, or GROK_MOE_F32 with fp32 activations).
+ * route_idx / route_gate: optional DEVICE arrays [T][k] (int32 expert
+ * indices, fp32 gates). When route_idx is non-NULL the router is skipped and
+ * this routing is used instead (router_w may then be NULL); each row must
+ * hold k distinct indices in [0, E) (an index outside that range is dropped
+ * and contributes nothing). */
+typedef struct grok_moe_args {
+  const void* x;
+  const void* router_w;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const float* scales;
+  void* out;
+  int64_t T, d, f;
+  int32_t E, k;
+  int32_t act_dtype, w_dtype;
+  const int32_t* route_idx;
+  const float* route_gate;
+} grok_moe_args;
+
+/* Optional outputs for tests and profiling (every field may be NULL).
+ * Device arrays receive copies of the intermediate results:
+ *   idx [T][k] int32, gate [T][k] fp32  - the routing
+ *   counts [E], offsets [E+1] int32     - rows per expert and their exclusive scan
+ *   perm [k*T] int32                    - row -> token (segment e in ascending token order)
+ *   pos [T][k] int32                    - (token, slot) -> row
+ * events: hipEvent_t handles; when events[i] is non-NULL it is recorded on the
+ * stream before stage i (0 router, 1 permutation, 2 gate/up GEMM, 3 down
+ * GEMM, 4 combine) and events[5] after the last stage. */
+typedef struct grok_moe_debug {
+  int32_t* idx;
+  float* gate;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* pos;
+  void* events[6];
+} grok_moe_debug;
+
+/* Bytes of device workspace grok_moe_forward_ex needs for this shape, or 0 for
+ * an invalid or unsupported shape. */
+size_t grok_moe_workspace_bytes(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t act_dtype,
+                                int32_t w_dtype);
+
+/* The layer with caller-owned workspace (ws: device memory, 256-byte aligned,
+ * at least grok_moe_workspace_bytes(); its contents on entry do not matter and
+ * are clobbered). dbg may be NULL. Allocates nothing. */
+int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const grok_moe_debug* dbg,
+                        void* stream);
+
+/* bf16 activations, bf16 router and bf16 expert weights. Takes its workspace
+ * from hipMallocAsync/hipFreeAsync on `stream` (stream-ordered). */
+int grok_moe_forward(const void* x, const void* router_w, const void* w_gate, const void* w_up,
+                     const void* w_down, void* out, int64_t T, int64_t d, int64_t f, int32_t E, int32_t k,
+                     void* stream);
+
+/* bf16 activations and router; 8-bit expert weights (int8 q in [-127, 127])
+ * with one fp32 scale per output channel (book ch. 1, section 1.2, INT8 box:
+ * int8 values plus a scale per group, dequantised at compute time). */
+int grok_moe_forward_w8(const void* x, const void* router_w, const int8_t* w_gate, const int8_t* w_up,
+                        const int8_t* w_down, const float* scales, void* out, int64_t T, int64_t d, int64_t f,
+                        int32_t E, int32_t k, void* stream);
+
+/* fp32 activations, router and expert weights (fp32 accumulation). */
+int grok_moe_forward_f32(const float* x, const float* router_w, const float* w_gate, const float* w_up,
+                         const float* w_down, float* out, int64_t T, int64_t d, int64_t f, int32_t E, int32_t k,
+                         void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* grok_moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GROK_MOE_H */

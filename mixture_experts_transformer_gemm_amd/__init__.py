@@ -1,0 +1,270 @@
+"""Python binding of the MI355X Grok-1 MoE feed-forward library (libgrok_moe.so).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+the library; torch supplies device memory and the current stream. The names
+mirror the C ABI in include/grok_moe.h, with the sizes taken from the tensor
+shapes:
+
+* ``grok_moe_forward``     bf16 activations and weights
+* ``grok_moe_forward_w8``  bf16 activations, int8 weights + fp32 per-channel scales
+* ``grok_moe_forward_f32`` fp32 everything
+* ``grok_moe_forward_ex``  any of the above with caller workspace, optional
+  routing override and debug outputs
+* ``grok_moe_workspace_bytes``, ``grok_moe_status_string``
+
+Layouts: x, out [T, d]; router_w [E, d]; w_gate, w_up [E, f, d]; w_down [E, d, f].
+If the library is not built, every call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgrok_moe.so")
+
+BF16, F32, I8 = 0, 1, 2
+OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
+STAGES = ("router", "permute", "gate_up", "down", "combine")
+
+EXPORTED = ("grok_moe_workspace_bytes", "grok_moe_forward_ex", "grok_moe_forward", "grok_moe_forward_w8",
+            "grok_moe_forward_f32", "grok_moe_status_string")
+
+
+class GrokMoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {grok_moe_status_string(code)} (status {code})")
+
+
+class Args(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("router_w", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
+                ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("T", ctypes.c_int64), ("d", ctypes.c_int64), ("f", ctypes.c_int64),
+                ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("w_dtype", ctypes.c_int32), ("route_idx", ctypes.c_void_p), ("route_gate", ctypes.c_void_p)]
+
+
+class Debug(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("gate", ctypes.c_void_p), ("counts", ctypes.c_void_p),
+                ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+                ("events", ctypes.c_void_p * 6)]
+
+
+_lib_handle = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                               "g.build()'` (hipcc, gfx950)")
+        h = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        h.grok_moe_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, i32]
+        h.grok_moe_workspace_bytes.restype = ctypes.c_size_t
+        h.grok_moe_forward_ex.argtypes = [ctypes.POINTER(Args), vp, ctypes.c_size_t, ctypes.POINTER(Debug), vp]
+        h.grok_moe_forward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
+        h.grok_moe_forward_w8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
+        h.grok_moe_forward_f32.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
+        for n in ("grok_moe_forward_ex", "grok_moe_forward", "grok_moe_forward_w8", "grok_moe_forward_f32"):
+            getattr(h, n).restype = ctypes.c_int
+        h.grok_moe_status_string.argtypes = [ctypes.c_int]
+        h.grok_moe_status_string.restype = ctypes.c_char_p
+        _lib_handle = h
+    return _lib_handle
+
+
+def grok_moe_status_string(code: int) -> str:
+    return lib().grok_moe_status_string(int(code)).decode()
+
+
+def grok_moe_workspace_bytes(T: int, d: int, f: int, E: int, k: int, act_dtype: int = BF16,
+                             w_dtype: int = BF16) -> int:
+    return int(lib().grok_moe_workspace_bytes(T, d, f, E, k, act_dtype, w_dtype))
+
+
+# ---------------------------------------------------------------- torch marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.int8:
+        return I8
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check_tensors(named: Dict[str, object]):
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _shape(x, w_gate, router_w):
+    T, d = x.shape
+    E, f, d2 = w_gate.shape
+    if d2 != d:
+        raise ValueError(f"w_gate is [E, f, d] with d={d2}, x has d={d}")
+    if router_w is not None and tuple(router_w.shape) != (E, d):
+        raise ValueError(f"router_w must be [E, d] = [{E}, {d}], got {tuple(router_w.shape)}")
+    return T, d, f, E
+
+
+def make_args(x, router_w, w_gate, w_up, w_down, out, k: int, scales=None, route_idx=None,
+              route_gate=None) -> Args:
+    T, d, f, E = _shape(x, w_gate, router_w)
+    if tuple(w_up.shape) != (E, f, d) or tuple(w_down.shape) != (E, d, f):
+        raise ValueError("w_up must be [E, f, d] and w_down [E, d, f]")
+    if tuple(out.shape) != (T, d):
+        raise ValueError("out must be [T, d]")
+    _check_tensors(dict(x=x, router_w=router_w, w_gate=w_gate, w_up=w_up, w_down=w_down, out=out, scales=scales,
+                        route_idx=route_idx, route_gate=route_gate))
+    a = Args()
+    a.x, a.router_w, a.w_gate, a.w_up, a.w_down = _ptr(x), _ptr(router_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down)
+    a.scales, a.out = _ptr(scales), _ptr(out)
+    a.T, a.d, a.f, a.E, a.k = T, d, f, E, k
+    a.act_dtype = _dtype_code(x)
+    a.w_dtype = _dtype_code(w_gate)
+    a.route_idx, a.route_gate = _ptr(route_idx), _ptr(route_gate)
+    return a
+
+
+def _raise(rc: int, where: str):
+    if rc != OK:
+        raise GrokMoeError(rc, where)
+
+
+def grok_moe_forward(x, router_w, w_gate, w_up, w_down, out=None, k: int = 2, stream=None):
+    """bf16 layer; allocates its workspace stream-ordered. Returns `out`."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(x)
+    T, d, f, E = _shape(x, w_gate, router_w)
+    _check_tensors(dict(x=x, router_w=router_w, w_gate=w_gate, w_up=w_up, w_down=w_down, out=out))
+    rc = lib().grok_moe_forward(_ptr(x), _ptr(router_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out), T, d,
+                                f, E, k, _stream(stream))
+    _raise(rc, "grok_moe_forward")
+    return out
+
+
+def grok_moe_forward_w8(x, router_w, w_gate, w_up, w_down, scales, out=None, k: int = 2, stream=None):
+    """bf16 activations, int8 weights, fp32 scales [gate E*f | up E*f | down E*d]. Returns `out`."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(x)
+    T, d, f, E = _shape(x, w_gate, router_w)
+    _check_tensors(dict(x=x, router_w=router_w, w_gate=w_gate, w_up=w_up, w_down=w_down, out=out, scales=scales))
+    rc = lib().grok_moe_forward_w8(_ptr(x), _ptr(router_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(scales),
+                                   _ptr(out), T, d, f, E, k, _stream(stream))
+    _raise(rc, "grok_moe_forward_w8")
+    return out
+
+
+def grok_moe_forward_f32(x, router_w, w_gate, w_up, w_down, out=None, k: int = 2, stream=None):
+    """fp32 layer. Returns `out`."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(x)
+    T, d, f, E = _shape(x, w_gate, router_w)
+    _check_tensors(dict(x=x, router_w=router_w, w_gate=w_gate, w_up=w_up, w_down=w_down, out=out))
+    rc = lib().grok_moe_forward_f32(_ptr(x), _ptr(router_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out), T,
+                                    d, f, E, k, _stream(stream))
+    _raise(rc, "grok_moe_forward_f32")
+    return out
+
+
+def grok_moe_forward_ex(x, router_w, w_gate, w_up, w_down, k: int = 2, scales=None, out=None, workspace=None,
+                        route_idx=None, route_gate=None, debug: bool = False,
+                        events: Optional[Sequence[object]] = None, stream=None):
+    """Layer with caller workspace. Returns (out, dbg) where dbg holds the routing intermediates
+    (idx, gate, counts, offsets, perm, pos) as device tensors when debug=True, else {}.
+    `events`: up to 6 raw hipEvent_t handles (see `HipEvents`) recorded before each stage and after the last."""
+    torch = _torch()
+    dev = x.device
+    if out is None:
+        out = torch.empty_like(x)
+    a = make_args(x, router_w, w_gate, w_up, w_down, out, k, scales, route_idx, route_gate)
+    need = grok_moe_workspace_bytes(a.T, a.d, a.f, a.E, a.k, a.act_dtype, a.w_dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    dbg = {}
+    dptr = None
+    if debug or events:
+        d = Debug()
+        if debug:
+            T, E = a.T, a.E
+            dbg = dict(idx=torch.full((T, k), -7, dtype=torch.int32, device=dev),
+                       gate=torch.full((T, k), -7.0, dtype=torch.float32, device=dev),
+                       counts=torch.full((E,), -7, dtype=torch.int32, device=dev),
+                       offsets=torch.full((E + 1,), -7, dtype=torch.int32, device=dev),
+                       perm=torch.full((T * k,), -7, dtype=torch.int32, device=dev),
+                       pos=torch.full((T, k), -7, dtype=torch.int32, device=dev))
+            for name, t in dbg.items():
+                setattr(d, name, t.data_ptr())
+        if events:
+            for i, ev in enumerate(events[:6]):
+                if ev:
+                    d.events[i] = ctypes.c_void_p(int(ev))
+        dptr = ctypes.byref(d)
+    rc = lib().grok_moe_forward_ex(ctypes.byref(a), workspace.data_ptr(), workspace.numel(), dptr,
+                                   _stream(stream))
+    _raise(rc, "grok_moe_forward_ex")
+    return out, dbg
+
+
+# ---------------------------------------------------------------- HIP events (timing plumbing)
+class HipEvents:
+    """A set of hipEvent_t handles made with the HIP runtime, for per-stage timing on any stream."""
+
+    def __init__(self, n: int):
+        self._rt = ctypes.CDLL("libamdhip64.so")
+        self._rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self._rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            rc = self._rt.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            self.handles.append(h.value)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        """Milliseconds between event i and event j (synchronises on event j)."""
+        self._rt.hipEventSynchronize(self.handles[j])
+        ms = ctypes.c_float()
+        rc = self._rt.hipEventElapsedTime(ctypes.byref(ms), self.handles[i], self.handles[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def close(self):
+        for h in self.handles:
+            self._rt.hipEventDestroy(h)
+        self.handles = []

@@ -1,0 +1,252 @@
+// C ABI of the MoE layer: argument validation, workspace layout, kernel
+// sequence. No kernel code lives here. See grok_moe.h for the contract.
+#include "grok_moe.h"
+#include "moe_internal.h"
+
+#include <string.h>
+
+using namespace gmoe;
+
+namespace {
+
+enum Path { PATH_F32 = 0, PATH_SKINNY = 1, PATH_TILED = 2 };
+
+constexpr int64_t kMaxT = int64_t(1) << 20;
+constexpr int64_t kMaxDim = int64_t(1) << 20;
+constexpr int kSkinnyMaxT = 128;
+
+struct Plan {
+  int path = 0;
+  int mt_max = 1;  // small-M path: rows per expert tile / 16
+  int splits = 1;  // split-K factor of the down projection
+  int64_t rows_cap = 0;
+  size_t off_idx = 0, off_gate = 0, off_counts = 0, off_offsets = 0, off_perm = 0, off_pos = 0;
+  size_t off_H = 0, off_Y = 0, total = 0;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int check_shape(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t act, int32_t wdt) {
+  if (T < 0 || d <= 0 || f <= 0 || E < 1 || k < 1 || k > E) return GROK_MOE_EINVAL;
+  const bool combo_ok = (act == GROK_MOE_BF16 && (wdt == GROK_MOE_BF16 || wdt == GROK_MOE_I8)) ||
+                        (act == GROK_MOE_F32 && wdt == GROK_MOE_F32);
+  if (!combo_ok) return GROK_MOE_EINVAL;
+  if (E > 64 || k > 8 || T > kMaxT || d > kMaxDim || f > kMaxDim) return GROK_MOE_EUNSUPPORTED;
+  if (act == GROK_MOE_F32) {
+    if (d % 8 || f % 4) return GROK_MOE_EUNSUPPORTED;
+  } else {
+    if (d % 128 || f % 256) return GROK_MOE_EUNSUPPORTED;
+  }
+  return GROK_MOE_OK;
+}
+
+Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t act) {
+  Plan p;
+  p.rows_cap = T * k;
+  if (act == GROK_MOE_F32) {
+    p.path = PATH_F32;
+  } else if (T <= kSkinnyMaxT) {
+    p.path = PATH_SKINNY;
+    const int64_t sub = (T + 15) / 16;  // rows of one expert <= T
+    p.mt_max = sub <= 1 ? 1 : sub <= 2 ? 2 : sub <= 4 ? 4 : 8;
+    // enough workgroups for the down projection to keep every CU streaming
+    int s = 1;
+    while (s < 8 && (int64_t)E * (d / 64) * s < 2048 && (f / (2 * s)) % 64 == 0) s *= 2;
+    p.splits = s;
+  } else {
+    p.path = PATH_TILED;
+  }
+  const size_t hsz = act == GROK_MOE_F32 ? 4 : 2;
+  size_t o = 0;
+  p.off_idx = o;     o = align256(o + sizeof(int32_t) * (size_t)(T * k));
+  p.off_gate = o;    o = align256(o + sizeof(float) * (size_t)(T * k));
+  p.off_counts = o;  o = align256(o + sizeof(int32_t) * 64);
+  p.off_offsets = o; o = align256(o + sizeof(int32_t) * 65);
+  p.off_perm = o;    o = align256(o + sizeof(int32_t) * (size_t)(T * k));
+  p.off_pos = o;     o = align256(o + sizeof(int32_t) * (size_t)(T * k));
+  p.off_H = o;       o = align256(o + hsz * (size_t)p.rows_cap * (size_t)f);
+  p.off_Y = o;       o = align256(o + sizeof(float) * (size_t)p.splits * (size_t)p.rows_cap * (size_t)d);
+  p.total = o;
+  return p;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int validate(const grok_moe_args* a) {
+  if (!a) return GROK_MOE_EINVAL;
+  int rc = check_shape(a->T, a->d, a->f, a->E, a->k, a->act_dtype, a->w_dtype);
+  if (rc != GROK_MOE_OK || a->T == 0) return rc;
+  if (!a->x || !a->out || !a->w_gate || !a->w_up || !a->w_down) return GROK_MOE_EINVAL;
+  if (a->route_idx) {
+    if (!a->route_gate) return GROK_MOE_EINVAL;
+  } else if (!a->router_w) {
+    return GROK_MOE_EINVAL;
+  }
+  if (a->w_dtype == GROK_MOE_I8 && !a->scales) return GROK_MOE_EINVAL;
+  const void* ptrs[] = {a->x, a->router_w, a->w_gate, a->w_up, a->w_down, a->scales, a->out,
+                        a->route_idx, a->route_gate};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GROK_MOE_EALIGN;
+  return GROK_MOE_OK;
+}
+
+#define GMOE_TRY(expr)                        \
+  do {                                        \
+    if ((expr) != hipSuccess) return GROK_MOE_EHIP; \
+  } while (0)
+
+int record(const grok_moe_debug* dbg, int i, hipStream_t st) {
+  if (dbg && dbg->events[i]) return hipEventRecord((hipEvent_t)dbg->events[i], st) == hipSuccess;
+  return 1;
+}
+
+int copy_out(void* dst, const void* src, size_t bytes, hipStream_t st) {
+  if (!dst || bytes == 0) return 1;
+  return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st) == hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t grok_moe_workspace_bytes(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t act_dtype,
+                                int32_t w_dtype) {
+  if (check_shape(T, d, f, E, k, act_dtype, w_dtype) != GROK_MOE_OK) return 0;
+  return make_plan(T, d, f, E, k, act_dtype).total;
+}
+
+int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const grok_moe_debug* dbg,
+                        void* stream) {
+  int rc = validate(a);
+  if (rc != GROK_MOE_OK) return rc;
+  if (a->T == 0) return GROK_MOE_OK;
+  const Plan p = make_plan(a->T, a->d, a->f, a->E, a->k, a->act_dtype);
+  if (!ws || ws_bytes < p.total) return GROK_MOE_EWORKSPACE;
+  if (((uintptr_t)ws & 255) != 0) return GROK_MOE_EALIGN;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* w = (char*)ws;
+  int32_t* idx = (int32_t*)(w + p.off_idx);
+  float* gate = (float*)(w + p.off_gate);
+  int32_t* counts = (int32_t*)(w + p.off_counts);
+  int32_t* offsets = (int32_t*)(w + p.off_offsets);
+  int32_t* perm = (int32_t*)(w + p.off_perm);
+  int32_t* pos = (int32_t*)(w + p.off_pos);
+  void* H = w + p.off_H;
+  float* Y = (float*)(w + p.off_Y);
+  const int64_t T = a->T;
+  const int d = (int)a->d, f = (int)a->f, E = a->E, k = a->k;
+  const int act_f32 = a->act_dtype == GROK_MOE_F32;
+  const int w8 = a->w_dtype == GROK_MOE_I8;
+
+  // stage 0: router
+  if (!record(dbg, 0, st)) return GROK_MOE_EHIP;
+  const int32_t* ridx = idx;
+  const float* rgate = gate;
+  if (a->route_idx) {
+    ridx = a->route_idx;
+    rgate = a->route_gate;
+  } else {
+    GMOE_TRY(launch_router(act_f32, a->x, a->router_w, T, d, E, k, idx, gate, st));
+  }
+  // stage 1: permutation
+  if (!record(dbg, 1, st)) return GROK_MOE_EHIP;
+  GMOE_TRY(launch_permute(ridx, T, E, k, counts, offsets, perm, pos, st));
+  const RouteView rv{counts, offsets, perm};
+
+  // stage 2: gate/up projections + GELU * up
+  if (!record(dbg, 2, st)) return GROK_MOE_EHIP;
+  if (p.path == PATH_F32) {
+    GMOE_TRY(launch_f32_gateup((const float*)a->x, rv, (const float*)a->w_gate, (const float*)a->w_up, T,
+                               p.rows_cap, d, f, E, (float*)H, st));
+  } else if (p.path == PATH_SKINNY) {
+    GMOE_TRY(launch_skinny_gateup(w8, p.mt_max, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, a->scales, T, d,
+                                  f, E, (bf16_bits*)H, st));
+  } else {
+    GMOE_TRY(launch_tiled_gateup(w8, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, a->scales, T, p.rows_cap, d,
+                                 f, E, (bf16_bits*)H, st));
+  }
+  // stage 3: down projection
+  if (!record(dbg, 3, st)) return GROK_MOE_EHIP;
+  if (p.path == PATH_F32) {
+    GMOE_TRY(launch_f32_down((const float*)H, rv, (const float*)a->w_down, p.rows_cap, d, f, E, Y, st));
+  } else if (p.path == PATH_SKINNY) {
+    GMOE_TRY(launch_skinny_down(w8, p.mt_max, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales,
+                                p.rows_cap, d, f, E, Y, st));
+  } else {
+    GMOE_TRY(launch_tiled_down(w8, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d, f, E, Y, st));
+  }
+  // stage 4: gate-weighted combine
+  if (!record(dbg, 4, st)) return GROK_MOE_EHIP;
+  GMOE_TRY(launch_combine(act_f32, Y, p.splits, p.rows_cap, pos, rgate, T, d, k, a->out, st));
+  if (!record(dbg, 5, st)) return GROK_MOE_EHIP;
+
+  if (dbg) {
+    const size_t tk = (size_t)(T * k);
+    if (!copy_out(dbg->idx, ridx, 4 * tk, st) || !copy_out(dbg->gate, rgate, 4 * tk, st) ||
+        !copy_out(dbg->counts, counts, 4 * (size_t)E, st) || !copy_out(dbg->offsets, offsets, 4 * (size_t)(E + 1), st) ||
+        !copy_out(dbg->perm, perm, 4 * tk, st) || !copy_out(dbg->pos, pos, 4 * tk, st))
+      return GROK_MOE_EHIP;
+  }
+  return GROK_MOE_OK;
+}
+
+static int forward_alloc(const grok_moe_args* a, void* stream) {
+  int rc = validate(a);
+  if (rc != GROK_MOE_OK) return rc;
+  if (a->T == 0) return GROK_MOE_OK;
+  const size_t bytes = grok_moe_workspace_bytes(a->T, a->d, a->f, a->E, a->k, a->act_dtype, a->w_dtype);
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, bytes, st) != hipSuccess) return GROK_MOE_EHIP;
+  rc = grok_moe_forward_ex(a, ws, bytes, nullptr, stream);
+  if (hipFreeAsync(ws, st) != hipSuccess && rc == GROK_MOE_OK) rc = GROK_MOE_EHIP;
+  return rc;
+}
+
+int grok_moe_forward(const void* x, const void* router_w, const void* w_gate, const void* w_up,
+                     const void* w_down, void* out, int64_t T, int64_t d, int64_t f, int32_t E, int32_t k,
+                     void* stream) {
+  grok_moe_args a;
+  memset(&a, 0, sizeof(a));
+  a.x = x; a.router_w = router_w; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down; a.out = out;
+  a.T = T; a.d = d; a.f = f; a.E = E; a.k = k;
+  a.act_dtype = GROK_MOE_BF16; a.w_dtype = GROK_MOE_BF16;
+  return forward_alloc(&a, stream);
+}
+
+int grok_moe_forward_w8(const void* x, const void* router_w, const int8_t* w_gate, const int8_t* w_up,
+                        const int8_t* w_down, const float* scales, void* out, int64_t T, int64_t d, int64_t f,
+                        int32_t E, int32_t k, void* stream) {
+  grok_moe_args a;
+  memset(&a, 0, sizeof(a));
+  a.x = x; a.router_w = router_w; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down; a.scales = scales;
+  a.out = out; a.T = T; a.d = d; a.f = f; a.E = E; a.k = k;
+  a.act_dtype = GROK_MOE_BF16; a.w_dtype = GROK_MOE_I8;
+  return forward_alloc(&a, stream);
+}
+
+int grok_moe_forward_f32(const float* x, const float* router_w, const float* w_gate, const float* w_up,
+                         const float* w_down, float* out, int64_t T, int64_t d, int64_t f, int32_t E, int32_t k,
+                         void* stream) {
+  grok_moe_args a;
+  memset(&a, 0, sizeof(a));
+  a.x = x; a.router_w = router_w; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down; a.out = out;
+  a.T = T; a.d = d; a.f = f; a.E = E; a.k = k;
+  a.act_dtype = GROK_MOE_F32; a.w_dtype = GROK_MOE_F32;
+  return forward_alloc(&a, stream);
+}
+
+const char* grok_moe_status_string(int status) {
+  switch (status) {
+    case GROK_MOE_OK: return "ok";
+    case GROK_MOE_EINVAL: return "invalid argument (null pointer, negative size, k > E or bad dtype)";
+    case GROK_MOE_EUNSUPPORTED: return "unsupported shape (E <= 64, k <= 8, d % 128 == 0, f % 256 == 0 for bf16/int8)";
+    case GROK_MOE_EALIGN: return "misaligned pointer (16-byte tensors, 256-byte workspace)";
+    case GROK_MOE_EWORKSPACE: return "workspace missing or too small";
+    case GROK_MOE_EHIP: return "HIP runtime call failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

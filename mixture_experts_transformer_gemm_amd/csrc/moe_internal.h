@@ -1,0 +1,74 @@
+// Internal declarations shared by the HIP translation units of the MoE layer.
+// Not part of the public ABI (that is include/grok_moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gmoe {
+
+// Raw bf16 values travel as uint16_t bit patterns.
+typedef uint16_t bf16_bits;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Round to nearest even (NaN inputs are outside the layer's contract).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two floats -> packed pair of bf16 (lo in the low half).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Exact-erf GELU: z * Phi(z) = z (1 + erf(z / sqrt 2)) / 2, with the device library's erff.
+__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+
+// Device view of the routing produced by the permutation stage.
+struct RouteView {
+  const int32_t* counts;   // [E] rows per expert
+  const int32_t* offsets;  // [E+1] first row of each expert segment
+  const int32_t* perm;     // [k*T] row -> token
+};
+
+// ---------------------------------------------------------------- launchers
+// All launchers enqueue on `stream` and return the launch status.
+
+hipError_t launch_router(int act_f32, const void* x, const void* router_w, int64_t T, int d, int E, int k,
+                         int32_t* idx, float* gate, hipStream_t stream);
+
+hipError_t launch_permute(const int32_t* idx, int64_t T, int E, int k, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* pos, hipStream_t stream);
+
+// out[t] = sum_s gate[t][s] * (sum_{p<S} Y[p][pos[t][s]]), Y: [S][rows_cap][d] fp32
+hipError_t launch_combine(int out_f32, const float* Y, int S, int64_t rows_cap, const int32_t* pos,
+                          const float* gate, int64_t T, int d, int k, void* out, hipStream_t stream);
+
+// Small-M path (every expert segment fits in one tile of 16*mt_max rows).
+hipError_t launch_skinny_gateup(int w8, int mt_max, const bf16_bits* x, RouteView rv, const void* wg,
+                                const void* wu, const float* scales, int64_t T, int d, int f, int E,
+                                bf16_bits* H, hipStream_t stream);
+hipError_t launch_skinny_down(int w8, int mt_max, int splits, const bf16_bits* H, RouteView rv, const void* wd,
+                              const float* scales, int64_t rows_cap, int d, int f, int E, float* Y,
+                              hipStream_t stream);
+
+// Large-M path (LDS-tiled MFMA grouped GEMM).
+hipError_t launch_tiled_gateup(int w8, const bf16_bits* x, RouteView rv, const void* wg, const void* wu,
+                               const float* scales, int64_t T, int64_t rows_cap, int d, int f, int E,
+                               bf16_bits* H, hipStream_t stream);
+hipError_t launch_tiled_down(int w8, const bf16_bits* H, RouteView rv, const void* wd, const float* scales,
+                             int64_t rows_cap, int d, int f, int E, float* Y, hipStream_t stream);
+
+// fp32 path (plain FMA kernels, fp32 accumulation).
+hipError_t launch_f32_gateup(const float* x, RouteView rv, const float* wg, const float* wu, int64_t T,
+                             int64_t rows_cap, int d, int f, int E, float* H, hipStream_t stream);
+hipError_t launch_f32_down(const float* H, RouteView rv, const float* wd, int64_t rows_cap, int d, int f, int E,
+                           float* Y, hipStream_t stream);
+
+}  // namespace gmoe

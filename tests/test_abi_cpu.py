@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments before anything touches a GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_transformer_gemm_amd as gm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "grok_moe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(grok_moe_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_binding_names():
+    decl = declared_functions()
+    assert decl == sorted(gm.EXPORTED), decl
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(gm.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_library_is_gfx950_code():
+    blob = open(gm.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        s = gm.grok_moe_status_string(code)
+        assert s and s != "unknown status"
+    assert gm.grok_moe_status_string(7) == "unknown status"
+
+
+def test_workspace_bytes():
+    # decode shape: idx/gate/perm/pos + H [16, f] bf16 + split-K Y partials
+    ws = gm.grok_moe_workspace_bytes(8, 6144, 32768, 8, 2)
+    assert ws >= 16 * 32768 * 2 + 16 * 6144 * 4
+    # prefill: H [16384, 32768] bf16 dominates
+    ws = gm.grok_moe_workspace_bytes(8192, 6144, 32768, 8, 2)
+    assert 16384 * 32768 * 2 <= ws < 16384 * 32768 * 2 + 16384 * 6144 * 4 + (1 << 20)
+    assert gm.grok_moe_workspace_bytes(0, 6144, 32768, 8, 2) > 0
+    # invalid / unsupported shapes report 0
+    assert gm.grok_moe_workspace_bytes(8, 6144, 32768, 8, 9) == 0          # k > E
+    assert gm.grok_moe_workspace_bytes(8, 6100, 32768, 8, 2) == 0          # d % 128
+    assert gm.grok_moe_workspace_bytes(8, 6144, 32768, 65, 2) == 0         # E > 64
+    assert gm.grok_moe_workspace_bytes(8, 6144, 32768, 8, 2, gm.F32, gm.BF16) == 0   # dtype combo
+
+
+def _args(**kw):
+    a = gm.Args()
+    base = dict(x=0x10000, router_w=0x20000, w_gate=0x30000, w_up=0x40000, w_down=0x50000, scales=None,
+                out=0x60000, T=8, d=256, f=512, E=8, k=2, act_dtype=gm.BF16, w_dtype=gm.BF16, route_idx=None,
+                route_gate=None)
+    base.update(kw)
+    for n, v in base.items():
+        setattr(a, n, v)
+    return a
+
+
+def _call(a, ws=0x1000000, ws_bytes=1 << 40):
+    # every case below is rejected before the first HIP call
+    return gm.lib().grok_moe_forward_ex(ctypes.byref(a), ws, ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), gm.EINVAL),
+    (dict(out=None), gm.EINVAL),
+    (dict(w_down=None), gm.EINVAL),
+    (dict(router_w=None), gm.EINVAL),
+    (dict(route_idx=0x70000), gm.EINVAL),            # routing override without gates
+    (dict(T=-1), gm.EINVAL),
+    (dict(k=0), gm.EINVAL),
+    (dict(k=9, E=8), gm.EINVAL),
+    (dict(E=0), gm.EINVAL),
+    (dict(act_dtype=gm.F32), gm.EINVAL),             # f32 activations with bf16 weights
+    (dict(act_dtype=5), gm.EINVAL),
+    (dict(w_dtype=gm.I8), gm.EINVAL),                # int8 without scales
+    (dict(E=65, k=2), gm.EUNSUPPORTED),
+    (dict(E=16, k=9), gm.EUNSUPPORTED),
+    (dict(d=200), gm.EUNSUPPORTED),
+    (dict(f=384), gm.EUNSUPPORTED),
+    (dict(T=(1 << 20) + 1), gm.EUNSUPPORTED),
+    (dict(x=0x10008), gm.EALIGN),
+    (dict(w_up=0x40004), gm.EALIGN),
+    (dict(out=0x60002), gm.EALIGN),
+])
+def test_validation_errors(kw, code):
+    assert _call(_args(**kw)) == code
+
+
+def test_workspace_errors():
+    a = _args()
+    need = gm.grok_moe_workspace_bytes(8, 256, 512, 8, 2)
+    assert _call(a, ws=0x1000000, ws_bytes=need - 1) == gm.EWORKSPACE
+    assert _call(a, ws=0, ws_bytes=need) == gm.EWORKSPACE
+    assert _call(a, ws=0x1000010, ws_bytes=need) == gm.EALIGN
+
+
+def test_zero_tokens_is_a_noop():
+    # T = 0: valid shape, nothing enqueued, OK returned even with null tensors
+    assert _call(_args(T=0, x=None, out=None), ws=0, ws_bytes=0) == gm.OK
+
+
+def test_f32_shapes():
+    a = _args(act_dtype=gm.F32, w_dtype=gm.F32, d=24, f=20)
+    assert _call(a, ws=0x1000000, ws_bytes=16) == gm.EWORKSPACE   # valid shape, reaches the workspace check
+    assert _call(_args(act_dtype=gm.F32, w_dtype=gm.F32, d=12)) == gm.EUNSUPPORTED
+
+
+def test_plain_entry_points_validate_first():
+    lib = gm.lib()
+    assert lib.grok_moe_forward(None, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000, 8, 256, 512, 8, 2, None) \
+        == gm.EINVAL
+    assert lib.grok_moe_forward_w8(0x10000, 0x20000, 0x30000, 0x40000, 0x50000, None, 0x60000, 8, 256, 512, 8, 2,
+                                   None) == gm.EINVAL
+    assert lib.grok_moe_forward_f32(0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000, 8, 10, 512, 8, 2,
+                                    None) == gm.EUNSUPPORTED
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(gm, "_lib_handle", None)
+    monkeypatch.setattr(gm, "LIB_PATH", "/nonexistent/libgrok_moe.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        gm.lib()

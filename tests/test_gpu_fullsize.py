@@ -1,0 +1,79 @@
+"""GPU parity at the Grok-1 layer's full sizes (d=6144, f=32768, E=8, k=2), in the
+launch configuration the bench times (grok_moe_forward_ex with a caller workspace).
+
+All tokens are checked for routing and permutation; outputs are compared with
+the oracle on every token for the decode workload and on a seeded sample that
+covers every expert (first and last row of each segment plus random tokens) for
+the larger ones.
+"""
+import gc
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from gpu_util import TOL, check_permutation, check_routing, normwise_err, run_layer
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_tokens(dbg, E, n_random, seed):
+    offs, perm = dbg["offsets"], dbg["perm"]
+    pick = []
+    for e in range(E):
+        if offs[e + 1] > offs[e]:
+            pick += [int(perm[offs[e]]), int(perm[offs[e + 1] - 1])]
+    T = dbg["idx"].shape[0]
+    pick += list(np.random.default_rng(seed).choice(T, size=min(n_random, T), replace=False))
+    return sorted(set(pick))
+
+
+def _run_and_check(name, n_random=8):
+    print(f"[fullsize] generating workload {name}", flush=True)
+    w = synthetic.make(name)
+    print(f"[fullsize] {name}: T={w.T} d={w.d} f={w.f} E={w.E} k={w.k} weights={w.w_dtype}", flush=True)
+    got, dbg = run_layer(w, torch)
+    probs, oidx, _ = oracle.route(w.x, w.router_w, w.k)
+    check_routing(dbg["idx"], dbg["gate"], probs)
+    mismatched = int(np.sum(np.any(dbg["idx"] != oidx, axis=1)))
+    assert mismatched == 0, f"{mismatched} tokens routed differently from the oracle"
+    check_permutation(dbg["idx"], dbg, w.E)
+    assert np.all(np.isfinite(got))
+    gates = np.take_along_axis(probs, dbg["idx"].astype(np.int64), 1)
+    tokens = None if w.T <= 8 else _sample_tokens(dbg, w.E, n_random, seed=w.T)
+    ref = oracle.forward_given_routing(w.x, w.w_gate, w.w_up, w.w_down, dbg["idx"], gates, scales=w.scales,
+                                       tokens=tokens)
+    sub = got if tokens is None else got[tokens]
+    err = normwise_err(sub, ref)
+    tol = TOL["i8" if w.w_dtype == "i8" else "bf16"]
+    print(f"[fullsize] {name}: {len(sub)} tokens checked, normwise error {err:.3e} (tol {tol})", flush=True)
+    assert err <= tol
+    counts = dbg["counts"].copy()
+    del w, got
+    gc.collect()
+    return dbg, counts
+
+
+def test_decode_full():
+    dbg, counts = _run_and_check("decode")
+    assert counts.sum() == 16
+
+
+def test_int8_full():
+    _run_and_check("int8", n_random=8)
+
+
+def test_skew_full():
+    dbg, counts = _run_and_check("skew", n_random=6)
+    share = counts / counts.sum()
+    assert share[0] > 0.4 and share[1] > 0.22
+
+
+def test_prefill_full():
+    dbg, counts = _run_and_check("prefill", n_random=6)
+    pairs = {tuple(sorted(p)) for p in dbg["idx"].tolist()}
+    assert len(pairs) == 28
+    assert counts.sum() == 2 * 8192
