@@ -40,7 +40,7 @@
  *    enqueues nothing and writes nothing.
  *  - `out` must not alias any input. T = 0 is a no-op that returns OK.
  *  - Supported shapes (GROK_MOE_EUNSUPPORTED otherwise): 1 <= k <= min(E, 8),
- *    E <= 64, bf16 and 8-bit weights need d % 128 == 0 and f % 256 == 0;
+ *    E <= 64, bf16 and 8-bit weights need d % 256 == 0 and f % 256 == 0;
  *    fp32 needs d % 8 == 0 and f % 4 == 0; T <= 2^20.
  *  - Pointers must be 16-byte aligned (GROK_MOE_EALIGN otherwise).
  *  - Thread-safe: no global mutable state. Concurrent calls on different

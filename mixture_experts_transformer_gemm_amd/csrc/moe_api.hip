@@ -13,12 +13,13 @@ enum Path { PATH_F32 = 0, PATH_SKINNY = 1, PATH_TILED = 2 };
 
 constexpr int64_t kMaxT = int64_t(1) << 20;
 constexpr int64_t kMaxDim = int64_t(1) << 20;
-constexpr int kSkinnyMaxT = 128;
+constexpr int kSkinnyMaxT = 64;
 
 struct Plan {
   int path = 0;
   int mt_max = 1;  // small-M path: rows per expert tile / 16
   int splits = 1;  // split-K factor of the down projection
+  int bm = 256;    // tiled path: rows per workgroup tile
   int64_t rows_cap = 0;
   size_t off_idx = 0, off_gate = 0, off_counts = 0, off_offsets = 0, off_perm = 0, off_pos = 0;
   size_t off_H = 0, off_Y = 0, total = 0;
@@ -35,7 +36,7 @@ int check_shape(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t a
   if (act == GROK_MOE_F32) {
     if (d % 8 || f % 4) return GROK_MOE_EUNSUPPORTED;
   } else {
-    if (d % 128 || f % 256) return GROK_MOE_EUNSUPPORTED;
+    if (d % 256 || f % 256) return GROK_MOE_EUNSUPPORTED;
   }
   return GROK_MOE_OK;
 }
@@ -48,13 +49,15 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ac
   } else if (T <= kSkinnyMaxT) {
     p.path = PATH_SKINNY;
     const int64_t sub = (T + 15) / 16;  // rows of one expert <= T
-    p.mt_max = sub <= 1 ? 1 : sub <= 2 ? 2 : sub <= 4 ? 4 : 8;
+    p.mt_max = sub <= 1 ? 1 : sub <= 2 ? 2 : 4;
     // enough workgroups for the down projection to keep every CU streaming
     int s = 1;
     while (s < 8 && (int64_t)E * (d / 64) * s < 2048 && (f / (2 * s)) % 64 == 0) s *= 2;
     p.splits = s;
   } else {
     p.path = PATH_TILED;
+    // about k*T/E rows per expert: the tile height that wastes little of it
+    p.bm = T <= 384 ? 64 : (T <= 1536 ? 128 : 256);
   }
   const size_t hsz = act == GROK_MOE_F32 ? 4 : 2;
   size_t o = 0;
@@ -163,7 +166,7 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
     GMOE_TRY(launch_skinny_gateup(w8, p.mt_max, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, a->scales, T, d,
                                   f, E, (bf16_bits*)H, st));
   } else {
-    GMOE_TRY(launch_tiled_gateup(w8, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, a->scales, T, p.rows_cap, d,
+    GMOE_TRY(launch_tiled_gateup(w8, p.bm, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, a->scales, T, p.rows_cap, d,
                                  f, E, (bf16_bits*)H, st));
   }
   // stage 3: down projection
@@ -174,7 +177,7 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
     GMOE_TRY(launch_skinny_down(w8, p.mt_max, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales,
                                 p.rows_cap, d, f, E, Y, st));
   } else {
-    GMOE_TRY(launch_tiled_down(w8, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d, f, E, Y, st));
+    GMOE_TRY(launch_tiled_down(w8, p.bm, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d, f, E, Y, st));
   }
   // stage 4: gate-weighted combine
   if (!record(dbg, 4, st)) return GROK_MOE_EHIP;
@@ -241,7 +244,7 @@ const char* grok_moe_status_string(int status) {
   switch (status) {
     case GROK_MOE_OK: return "ok";
     case GROK_MOE_EINVAL: return "invalid argument (null pointer, negative size, k > E or bad dtype)";
-    case GROK_MOE_EUNSUPPORTED: return "unsupported shape (E <= 64, k <= 8, d % 128 == 0, f % 256 == 0 for bf16/int8)";
+    case GROK_MOE_EUNSUPPORTED: return "unsupported shape (E <= 64, k <= 8, d % 256 == 0, f % 256 == 0 for bf16/int8)";
     case GROK_MOE_EALIGN: return "misaligned pointer (16-byte tensors, 256-byte workspace)";
     case GROK_MOE_EWORKSPACE: return "workspace missing or too small";
     case GROK_MOE_EHIP: return "HIP runtime call failed";

@@ -1,0 +1,83 @@
+// Device-side helpers shared by the GEMM translation units (internal).
+#pragma once
+
+#include "moe_internal.h"
+
+namespace gmoe {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// 4 signed bytes -> 4 bf16 (exact: |q| <= 127 needs 7 significant bits)
+__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, int sh) {
+  const float a = (float)(int)(int8_t)(w >> sh);
+  const float b = (float)(int)(int8_t)(w >> (sh + 8));
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+}
+// 16 int8 (one 16-byte load) -> two fragments of 8 bf16
+__device__ __forceinline__ void i8x16_to_frags(u32x4 q, u32x4& lo, u32x4& hi) {
+  lo.x = i8x2_to_bf16x2(q.x, 0);
+  lo.y = i8x2_to_bf16x2(q.x, 16);
+  lo.z = i8x2_to_bf16x2(q.y, 0);
+  lo.w = i8x2_to_bf16x2(q.y, 16);
+  hi.x = i8x2_to_bf16x2(q.z, 0);
+  hi.y = i8x2_to_bf16x2(q.z, 16);
+  hi.z = i8x2_to_bf16x2(q.w, 0);
+  hi.w = i8x2_to_bf16x2(q.w, 16);
+}
+
+// Reduction offset (within a 64-wide block) of the 8 values lane group g
+// supplies to MFMA step s. bf16 weights: step s covers [32s, 32s+32), so one
+// load instruction reads 64 contiguous bytes of each of 16 weight rows.
+// 8-bit weights: group g owns [16g, 16g+16), one 16-byte load, split in two.
+template <bool W8>
+__device__ __forceinline__ int koff(int s, int g) {
+  return W8 ? 16 * g + 8 * s : 32 * s + 8 * g;
+}
+
+// Loads the two weight fragments (steps 0 and 1) of one 64-wide block.
+template <bool W8>
+__device__ __forceinline__ void load_wfrags(const void* wrow, int kb, int g, u32x4& f0, u32x4& f1) {
+  if (W8) {
+    const u32x4 q = ld16((const int8_t*)wrow + kb + 16 * g);
+    i8x16_to_frags(q, f0, f1);
+  } else {
+    const bf16_bits* p = (const bf16_bits*)wrow + kb;
+    f0 = ld16(p + koff<false>(0, g));
+    f1 = ld16(p + koff<false>(1, g));
+  }
+}
+
+// Finds the M tile `mt` (tiles of BM rows, experts in order). Returns the
+// expert or -1 when mt is past the last tile.
+template <int BM>
+__device__ __forceinline__ int find_tile(const RouteView& rv, int E, int mt, int& m0, int& M) {
+  int acc = 0;
+  for (int q = 0; q < E; ++q) {
+    const int c = rv.counts[q];
+    const int nt = (c + BM - 1) / BM;
+    if (mt < acc + nt) {
+      const int mloc = (mt - acc) * BM;
+      m0 = rv.offsets[q] + mloc;
+      M = min(BM, c - mloc);
+      return q;
+    }
+    acc += nt;
+  }
+  return -1;
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+}  // namespace gmoe

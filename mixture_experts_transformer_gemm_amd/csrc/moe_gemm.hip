@@ -18,77 +18,9 @@
 // result register v of lane l is C[4g + v][l mod 16]. The 8 reduction values
 // a lane supplies are taken from the same reduction indices for both
 // operands, so the pairing is exact whatever order the hardware sums in.
-#include "moe_internal.h"
+#include "moe_device.h"
 
 namespace gmoe {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                 0, 0, 0);
-}
-
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-// 4 signed bytes -> 4 bf16 (exact: |q| <= 127 needs 7 significant bits)
-__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, int sh) {
-  const float a = (float)(int)(int8_t)(w >> sh);
-  const float b = (float)(int)(int8_t)(w >> (sh + 8));
-  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
-}
-// 16 int8 (one 16-byte load) -> two fragments of 8 bf16
-__device__ __forceinline__ void i8x16_to_frags(u32x4 q, u32x4& lo, u32x4& hi) {
-  lo.x = i8x2_to_bf16x2(q.x, 0);
-  lo.y = i8x2_to_bf16x2(q.x, 16);
-  lo.z = i8x2_to_bf16x2(q.y, 0);
-  lo.w = i8x2_to_bf16x2(q.y, 16);
-  hi.x = i8x2_to_bf16x2(q.z, 0);
-  hi.y = i8x2_to_bf16x2(q.z, 16);
-  hi.z = i8x2_to_bf16x2(q.w, 0);
-  hi.w = i8x2_to_bf16x2(q.w, 16);
-}
-
-// Reduction offset (within a 64-wide block) of the 8 values lane group g
-// supplies to MFMA step s. bf16 weights: step s covers [32s, 32s+32), so one
-// load instruction reads 64 contiguous bytes of each of 16 weight rows.
-// 8-bit weights: group g owns [16g, 16g+16), one 16-byte load, split in two.
-template <bool W8>
-__device__ __forceinline__ int koff(int s, int g) {
-  return W8 ? 16 * g + 8 * s : 32 * s + 8 * g;
-}
-
-// Loads the two weight fragments (steps 0 and 1) of one 64-wide block.
-template <bool W8>
-__device__ __forceinline__ void load_wfrags(const void* wrow, int kb, int g, u32x4& f0, u32x4& f1) {
-  if (W8) {
-    const u32x4 q = ld16((const int8_t*)wrow + kb + 16 * g);
-    i8x16_to_frags(q, f0, f1);
-  } else {
-    const bf16_bits* p = (const bf16_bits*)wrow + kb;
-    f0 = ld16(p + koff<false>(0, g));
-    f1 = ld16(p + koff<false>(1, g));
-  }
-}
-
-// Finds the M tile `mt` (tiles of BM rows, experts in order). Returns the
-// expert or -1 when mt is past the last tile.
-template <int BM>
-__device__ __forceinline__ int find_tile(const RouteView& rv, int E, int mt, int& m0, int& M) {
-  int acc = 0;
-  for (int q = 0; q < E; ++q) {
-    const int c = rv.counts[q];
-    const int nt = (c + BM - 1) / BM;
-    if (mt < acc + nt) {
-      const int mloc = (mt - acc) * BM;
-      m0 = rv.offsets[q] + mloc;
-      M = min(BM, c - mloc);
-      return q;
-    }
-    acc += nt;
-  }
-  return -1;
-}
 
 // =====================================================================
 // Small-M path. Every expert segment has at most 16*MT rows (M_e <= T).
@@ -320,208 +252,6 @@ hipError_t launch_skinny_down(int w8, int mt_max, int splits, const bf16_bits* H
   }
 #undef GMOE_SD
   return hipErrorInvalidValue;
-}
-
-// =====================================================================
-// Large-M path: LDS-tiled grouped GEMM. Tile BM x BN x 64 per workgroup of
-// 4 wavefronts in a 2 x 2 layout (each wavefront 64 rows x 64 channels per
-// weight matrix). LDS rows hold 64 bf16 = 8 chunks of 16 bytes, chunk c of
-// row r stored at position c ^ (r mod 8) so that the 16 lanes reading one
-// fragment column hit distinct bank groups. Global loads for tile k+1 are
-// issued before the MFMAs of tile k. 8-bit weights are widened to bf16 on
-// their way into LDS.
-// =====================================================================
-constexpr int TBM = 128, TBN = 128, TBK = 64;
-
-__device__ __forceinline__ int swz(int r, int c) { return (r * 8 + (c ^ (r & 7))) * 8; }  // element offset
-
-template <bool GATEUP, bool W8>
-__global__ __launch_bounds__(256) void tiled_kernel(const bf16_bits* __restrict__ A, RouteView rv,
-                                                    const void* __restrict__ w0, const void* __restrict__ w1,
-                                                    const float* __restrict__ scales, int64_t T, int K, int N,
-                                                    int E, int Ftot, void* __restrict__ out) {
-  constexpr int NW = GATEUP ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) bf16_bits sW[NW][TBN * TBK];
-  __shared__ __attribute__((aligned(16))) bf16_bits sA[TBM * TBK];
-
-  const int nN = N / TBN;
-  const int mt = blockIdx.x / nN;
-  const int nt = blockIdx.x - mt * nN;
-  int m0 = 0, M = 0;
-  const int e = find_tile<TBM>(rv, E, mt, m0, M);
-  if (e < 0) return;
-  const int n0 = nt * TBN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int wn = wave & 1, wm = wave >> 1;
-  const size_t wsz = W8 ? 1 : 2;
-
-  // global -> LDS assignment (bf16 tiles): chunk lc of rows lr + 32p
-  const int lc = tid & 7, lr = tid >> 3;
-  const bf16_bits* arow[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    int r = lr + 32 * p;
-    if (r >= M) r = M - 1;
-    if (GATEUP) {
-      int tok = rv.perm[m0 + r];
-      tok = tok < 0 ? 0 : (tok >= T ? (int)(T - 1) : tok);
-      arow[p] = A + (int64_t)tok * K;
-    } else {
-      arow[p] = A + (int64_t)(m0 + r) * K;
-    }
-  }
-  // weights: bf16 -> same mapping as A; int8 -> 4 chunks of 16 bytes per row, rows tid/4 + 64p
-  const int qc = tid & 3, qr = tid >> 2;
-  const char* wbase[NW];
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const char* base = (const char*)(w == 0 ? w0 : w1);
-    wbase[w] = base + ((int64_t)e * N + n0) * (int64_t)K * wsz;
-  }
-
-  u32x4 ra[4];
-  u32x4 rw[NW][4];
-  auto gload = [&](int kb) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) ra[p] = ld16(arow[p] + kb + lc * 8);
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      if (W8) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-          rw[w][p] = ld16(wbase[w] + (int64_t)(qr + 64 * p) * K + kb + qc * 16);
-      } else {
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-          rw[w][p] = ld16((const bf16_bits*)wbase[w] + (int64_t)(lr + 32 * p) * K + kb + lc * 8);
-      }
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) *reinterpret_cast<u32x4*>(&sA[swz(lr + 32 * p, lc)]) = ra[p];
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      if (W8) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          u32x4 lo, hi;
-          i8x16_to_frags(rw[w][p], lo, hi);
-          const int r = qr + 64 * p;
-          *reinterpret_cast<u32x4*>(&sW[w][swz(r, 2 * qc)]) = lo;
-          *reinterpret_cast<u32x4*>(&sW[w][swz(r, 2 * qc + 1)]) = hi;
-        }
-      } else {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) *reinterpret_cast<u32x4*>(&sW[w][swz(lr + 32 * p, lc)]) = rw[w][p];
-      }
-    }
-  };
-
-  f32x4 acc[NW][4][4];
-#pragma unroll
-  for (int w = 0; w < NW; ++w)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[w][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = K / TBK;
-  gload(0);
-  lstore();
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload((kt + 1) * TBK);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int c = 4 * s + g;
-      u32x4 xa[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const u32x4*>(&sA[swz(wm * 64 + j * 16 + r16, c)]);
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4 wa = *reinterpret_cast<const u32x4*>(&sW[w][swz(wn * 64 + i * 16 + r16, c)]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[w][i][j] = mfma16(wa, xa[j], acc[w][i][j]);
-        }
-      }
-    }
-    __syncthreads();
-    if (kt + 1 < nk) {
-      lstore();
-      __syncthreads();
-    }
-  }
-
-  // epilogue: lane owns channels n0 + wn*64 + i*16 + 4g .. +3 of row wm*64 + j*16 + r16
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int nc = n0 + wn * 64 + i * 16 + 4 * g;
-    float s0[4] = {1.f, 1.f, 1.f, 1.f}, s1[4] = {1.f, 1.f, 1.f, 1.f};
-    if (W8) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        if (GATEUP) {
-          s0[v] = scales[(int64_t)e * N + nc + v];
-          s1[v] = scales[(int64_t)E * N + (int64_t)e * N + nc + v];
-        } else {
-          s0[v] = scales[2 * (int64_t)E * Ftot + (int64_t)e * N + nc + v];
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = wm * 64 + j * 16 + r16;
-      if (m < M) {
-        if (GATEUP) {
-          float h[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) h[v] = gelu_erf(acc[0][i][j][v] * s0[v]) * (acc[NW - 1][i][j][v] * s1[v]);
-          uint2 o;
-          o.x = pack_bf16x2(h[0], h[1]);
-          o.y = pack_bf16x2(h[2], h[3]);
-          *reinterpret_cast<uint2*>((bf16_bits*)out + (int64_t)(m0 + m) * N + nc) = o;
-        } else {
-          float4 o = make_float4(acc[0][i][j][0] * s0[0], acc[0][i][j][1] * s0[1], acc[0][i][j][2] * s0[2],
-                                 acc[0][i][j][3] * s0[3]);
-          *reinterpret_cast<float4*>((float*)out + (int64_t)(m0 + m) * N + nc) = o;
-        }
-      }
-    }
-  }
-}
-
-static unsigned tiled_blocks(int64_t rows_cap, int E, int N) {
-  const int64_t mt_ub = rows_cap / TBM + E;
-  return (unsigned)(mt_ub * (N / TBN));
-}
-
-hipError_t launch_tiled_gateup(int w8, const bf16_bits* x, RouteView rv, const void* wg, const void* wu,
-                               const float* scales, int64_t T, int64_t rows_cap, int d, int f, int E,
-                               bf16_bits* H, hipStream_t st) {
-  const dim3 grid(tiled_blocks(rows_cap, E, f));
-  if (w8)
-    hipLaunchKernelGGL((tiled_kernel<true, true>), grid, dim3(256), 0, st, x, rv, wg, wu, scales, T, d, f, E, f,
-                       (void*)H);
-  else
-    hipLaunchKernelGGL((tiled_kernel<true, false>), grid, dim3(256), 0, st, x, rv, wg, wu, scales, T, d, f, E, f,
-                       (void*)H);
-  return hipGetLastError();
-}
-
-hipError_t launch_tiled_down(int w8, const bf16_bits* H, RouteView rv, const void* wd, const float* scales,
-                             int64_t rows_cap, int d, int f, int E, float* Y, hipStream_t st) {
-  const dim3 grid(tiled_blocks(rows_cap, E, d));
-  if (w8)
-    hipLaunchKernelGGL((tiled_kernel<false, true>), grid, dim3(256), 0, st, H, rv, wd, wd, scales, rows_cap, f, d,
-                       E, f, (void*)Y);
-  else
-    hipLaunchKernelGGL((tiled_kernel<false, false>), grid, dim3(256), 0, st, H, rv, wd, wd, scales, rows_cap, f,
-                       d, E, f, (void*)Y);
-  return hipGetLastError();
 }
 
 // =====================================================================

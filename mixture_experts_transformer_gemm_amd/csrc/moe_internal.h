@@ -59,10 +59,11 @@ hipError_t launch_skinny_down(int w8, int mt_max, int splits, const bf16_bits* H
                               hipStream_t stream);
 
 // Large-M path (LDS-tiled MFMA grouped GEMM).
-hipError_t launch_tiled_gateup(int w8, const bf16_bits* x, RouteView rv, const void* wg, const void* wu,
+// bm: rows per workgroup tile (64, 128 or 256).
+hipError_t launch_tiled_gateup(int w8, int bm, const bf16_bits* x, RouteView rv, const void* wg, const void* wu,
                                const float* scales, int64_t T, int64_t rows_cap, int d, int f, int E,
                                bf16_bits* H, hipStream_t stream);
-hipError_t launch_tiled_down(int w8, const bf16_bits* H, RouteView rv, const void* wd, const float* scales,
+hipError_t launch_tiled_down(int w8, int bm, const bf16_bits* H, RouteView rv, const void* wd, const float* scales,
                              int64_t rows_cap, int d, int f, int E, float* Y, hipStream_t stream);
 
 // fp32 path (plain FMA kernels, fp32 accumulation).

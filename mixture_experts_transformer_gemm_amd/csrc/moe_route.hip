@@ -39,24 +39,27 @@ __device__ __forceinline__ void load8_f64(const float* p, double* o) {
   o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
 }
 
-// One wavefront per token. Lane e ends up holding logit e; softmax and the
-// k-fold arg-max run across lanes. Experts are processed 8 at a time.
+// One workgroup (4 wavefronts) per token, so the d-long dot products are
+// spread over 256 lanes and their loads are all in flight together. Each lane
+// accumulates 8 experts at a time over its 8-element chunks; the partials are
+// summed across lanes (butterfly) and across the 4 wavefronts (LDS, fixed
+// order). Wavefront 0 then holds logit e in lane e; softmax and the k-fold
+// arg-max run across its lanes.
 template <typename XT>
 __global__ __launch_bounds__(256) void router_topk_kernel(const XT* __restrict__ x, const XT* __restrict__ wr,
                                                           int64_t T, int d, int E, int k,
                                                           int32_t* __restrict__ idx, float* __restrict__ gate) {
+  __shared__ double s_part[4][64];
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int wave = threadIdx.x >> 6;
   const int nchunk = d >> 3;
-  for (int64_t t = wave; t < T; t += nwaves) {
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
     const XT* xr = x + t * (int64_t)d;
-    double my_logit = 0.0;
     for (int e0 = 0; e0 < E; e0 += 8) {
       double acc[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] = 0.0;
-      for (int c = lane; c < nchunk; c += 64) {
+      for (int c = threadIdx.x; c < nchunk; c += 256) {
         double xv[8];
         load8_f64(xr + c * 8, xv);
 #pragma unroll
@@ -71,42 +74,47 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const XT* __restrict__
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        double s = wave_sum_f64(acc[j]);
-        if (lane == e0 + j) my_logit = s;
+        const double s = wave_sum_f64(acc[j]);
+        if (lane == 0 && e0 + j < E) s_part[wave][e0 + j] = s;
       }
     }
-    const bool live = lane < E;
-    const double mx = wave_max_f64(live ? my_logit : -INFINITY);
-    const double ex = live ? exp(my_logit - mx) : 0.0;
-    const double z = wave_sum_f64(ex);
-    const double p = ex / z;
-    bool taken = false;
-    for (int s = 0; s < k; ++s) {
-      // arg-max of p over the experts not yet taken; key (p desc, index asc)
-      double pv = (live && !taken) ? p : -1.0;
-      int bi = lane;
+    __syncthreads();
+    if (wave == 0) {
+      const bool live = lane < E;
+      const double my_logit = live ? ((s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane])) : 0.0;
+      const double mx = wave_max_f64(live ? my_logit : -INFINITY);
+      const double ex = live ? exp(my_logit - mx) : 0.0;
+      const double z = wave_sum_f64(ex);
+      const double p = ex / z;
+      bool taken = false;
+      for (int s = 0; s < k; ++s) {
+        // arg-max of p over the experts not yet taken; key (p desc, index asc)
+        double pv = (live && !taken) ? p : -1.0;
+        int bi = lane;
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const double po = __shfl_xor(pv, off, 64);
-        const int io = __shfl_xor(bi, off, 64);
-        if (po > pv || (po == pv && io < bi)) {
-          pv = po;
-          bi = io;
+        for (int off = 32; off > 0; off >>= 1) {
+          const double po = __shfl_xor(pv, off, 64);
+          const int io = __shfl_xor(bi, off, 64);
+          if (po > pv || (po == pv && io < bi)) {
+            pv = po;
+            bi = io;
+          }
+        }
+        if (lane == bi) taken = true;
+        if (lane == 0) {
+          idx[t * k + s] = bi;
+          gate[t * k + s] = (float)pv;
         }
       }
-      if (lane == bi) taken = true;
-      if (lane == 0) {
-        idx[t * k + s] = bi;
-        gate[t * k + s] = (float)pv;
-      }
     }
+    __syncthreads();
   }
 }
 
 hipError_t launch_router(int act_f32, const void* x, const void* router_w, int64_t T, int d, int E, int k,
                          int32_t* idx, float* gate, hipStream_t stream) {
-  int64_t blocks = (T + 3) / 4;
-  if (blocks > 8192) blocks = 8192;
+  int64_t blocks = T;
+  if (blocks > 16384) blocks = 16384;
   if (blocks < 1) blocks = 1;
   if (act_f32)
     hipLaunchKernelGGL(router_topk_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,

@@ -89,6 +89,7 @@ def _call(a, ws=0x1000000, ws_bytes=1 << 40):
     (dict(E=65, k=2), gm.EUNSUPPORTED),
     (dict(E=16, k=9), gm.EUNSUPPORTED),
     (dict(d=200), gm.EUNSUPPORTED),
+    (dict(d=384), gm.EUNSUPPORTED),
     (dict(f=384), gm.EUNSUPPORTED),
     (dict(T=(1 << 20) + 1), gm.EUNSUPPORTED),
     (dict(x=0x10008), gm.EALIGN),

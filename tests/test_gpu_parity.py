@@ -45,7 +45,7 @@ def test_bf16_layer_small(T):
     _full_check(w)
 
 
-@pytest.mark.parametrize("T,d,f", [(3, 128, 256), (48, 384, 768), (200, 384, 768)])
+@pytest.mark.parametrize("T,d,f", [(3, 512, 256), (48, 512, 768), (200, 512, 768), (300, 768, 1280), (600, 256, 256)])
 def test_bf16_layer_other_shapes(T, d, f):
     w = synthetic.make("decode", T=T, d=d, f=f, seed=100 + T)
     _full_check(w)
