@@ -32,9 +32,15 @@
 // weight tiles through its L2.
 #include "moe_device.h"
 
+#include <type_traits>
+
 namespace gmoe {
 
 constexpr int TBN = 256;
+
+#ifndef GMOE_DMA_SB
+#define GMOE_DMA_SB 64
+#endif
 constexpr int kGroupM = 8;
 
 template <int BM, int NW = 4>
@@ -190,26 +196,36 @@ __device__ __forceinline__ void zero_acc(AccT<BM, NW>& acc) {
 // =====================================================================
 // bf16 weights: LDS filled by global_load_lds_dwordx4.
 //
-// Stage = 32 reduction values; an LDS row holds them in 4 chunks of 16 bytes
-// (64 bytes). Chunk c of LDS row R sits at slot c ^ ((R >> 2) & 3): measured
-// on gfx950 (one 1 KB ds_read_b128 per 4 clocks when conflict-free), this
-// keeps the fragment reads (lane l: row l mod 32, chunk c + l / 32)
-// conflict-free, where an XOR with the low row bits halves the rate.
-// One wavefront load instruction fills 16 LDS rows (1 KB): lane i writes row
-// 16 t + i / 4, slot i mod 4, so it fetches chunk (i mod 4) ^ g(row).
+// A stage holds SB reduction values of every tile row: SB = 32 gives 64-byte
+// LDS rows (4 chunks of 16 bytes), SB = 64 gives 128-byte rows (8 chunks),
+// i.e. whole 128-byte lines of each global row per stage. NS LDS stages;
+// the loads of stage k+NS-1 are issued at the start of stage k. One
+// wavefront load instruction fills 1 KB of LDS: lane i writes row
+// (1024 / row bytes) t + i / chunks, slot i mod chunks, so it fetches the
+// chunk that belongs in that slot.
+//
+// Slots (measured on gfx950, where a conflict-free 1 KB ds_read_b128 takes 4
+// clocks): 64-byte rows put chunk c of row R at c ^ ((R >> 2) & 3); 128-byte
+// rows at c ^ (R & 7) ^ ((R >> 3) & 1). Both keep the fragment reads (lane
+// l: row l mod 32, chunk c + l / 32) free of bank conflicts.
 // =====================================================================
-constexpr int DBK = 32;
-constexpr int DSTAGES = 4;
-
-template <int BM, int NW>
+template <int BM, int NW, int SB, int NS>
 struct DmaCfg {
   static constexpr int RT = BM + TBN;          // LDS rows per stage (activations, then weights)
-  static constexpr int Q = RT / (16 * NW);     // load instructions per wavefront per stage
-  static constexpr int kStageBytes = RT * 64;
-  static constexpr int kLdsBytes = DSTAGES * kStageBytes;
+  static constexpr int ROWB = SB * 2;          // bytes per LDS row
+  static constexpr int CH = ROWB / 16;         // 16-byte chunks per row
+  static constexpr int RPI = 1024 / ROWB;      // rows per load instruction
+  static constexpr int Q = RT / (RPI * NW);    // load instructions per wavefront per stage
+  static constexpr int STEPS = SB / 16;        // MFMA steps per stage
+  static constexpr int kStageBytes = RT * ROWB;
+  static constexpr int kLdsBytes = NS * kStageBytes;
 };
 
-__device__ __forceinline__ int dslot(int R, int c) { return c ^ ((R >> 2) & 3); }
+template <int SB>
+__device__ __forceinline__ int dslot(int R, int c) {
+  if (SB == 32) return c ^ ((R >> 2) & 3);
+  return c ^ (R & 7) ^ ((R >> 3) & 1);
+}
 
 // 16 bytes per lane from global memory straight into LDS: lane i of the
 // wavefront writes lds_base + 16 i (lds_base must be wavefront-uniform).
@@ -232,13 +248,13 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ __volatile__("" ::: "memory");
 }
 
-template <int BM, bool GATEUP, int NW>
+template <int BM, bool GATEUP, int NW, int SB, int NS>
 __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __restrict__ A, RouteView rv,
                                                      const void* __restrict__ w0, const void* __restrict__ w1,
                                                      int64_t T, int K, int N, int E, int Ftot,
                                                      void* __restrict__ out) {
   using C = TileCfg<BM, NW>;
-  using D = DmaCfg<BM, NW>;
+  using D = DmaCfg<BM, NW, SB, NS>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   Tile t;
   if (!select_tile<BM, GATEUP>(rv, E, N, t)) return;
@@ -251,8 +267,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
   const char* src[D::Q];
 #pragma unroll
   for (int q = 0; q < D::Q; ++q) {
-    const int R = 16 * (q * NW + wave) + (lane >> 2);
-    const int c = dslot(R, lane & 3);
+    const int R = D::RPI * (q * NW + wave) + lane / D::CH;
+    const int c = dslot<SB>(R, lane % D::CH);
     const char* row = R < BM ? (const char*)act_row<GATEUP>(A, rv, t, T, K, R)
                              : weight_row<GATEUP>(w0, w1, t, N, K, 2, R - BM);
     src[q] = row + c * 16;
@@ -260,81 +276,106 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
   auto issue = [&](int stage, int buf) {
     char* dst = lds + buf * D::kStageBytes;
 #pragma unroll
-    for (int q = 0; q < D::Q; ++q)
-      dma16(src[q] + (size_t)stage * (DBK * 2), dst + (q * NW + wave) * 1024);
-  };
-  auto read_frags = [&](int buf, int s, u32x4* wa, u32x4* xa) {
-    const char* b = lds + buf * D::kStageBytes;
-    const int c = 2 * s + hg;
-#pragma unroll
-    for (int i = 0; i < C::TI; ++i) {
-      const int R = BM + wtile_row<BM, GATEUP, NW>(wn, i) + r32;
-      wa[i] = *reinterpret_cast<const u32x4*>(b + R * 64 + dslot(R, c) * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < C::TJ; ++j) {
-      const int R = wm * C::RW + j * 32 + r32;
-      xa[j] = *reinterpret_cast<const u32x4*>(b + R * 64 + dslot(R, c) * 16);
-    }
+    for (int q = 0; q < D::Q; ++q) dma16(src[q] + (size_t)stage * D::ROWB, dst + (q * NW + wave) * 1024);
   };
 
   f32x16 acc[C::TI][C::TJ];
   zero_acc<BM, NW>(acc);
   u32x4 fw[2][C::TI], fx[2][C::TJ];
-  auto mfma_step = [&](int b) {
-#pragma unroll
-    for (int i = 0; i < C::TI; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TJ; ++j) acc[i][j] = mfma32(fw[b][i], fx[b][j], acc[i][j]);
-  };
+  const int nk = K / SB;
 
-  const int nk = K / DBK;
-  // prologue: stages 0..2 in flight (indices past the end re-read the last
-  // stage, in bounds, into buffers nobody reads)
+  // The stage loop, for a wavefront whose first TJV row subtiles (of 32 rows)
+  // hold rows of the segment: the others are past its end and get neither
+  // fragment reads nor MFMAs (a nearly empty last tile of an expert costs its
+  // loads, not a tile of MFMAs). Every instance has the same loads and
+  // barriers, so the wavefronts of a workgroup stay in step.
+  auto stage_loop = [&](auto tjv_tag) {
+    constexpr int TJV = decltype(tjv_tag)::value;
+    auto frags = [&](int buf, int s, u32x4* wa, u32x4* xa) {
+      if constexpr (TJV > 0) {
+        const char* b = lds + buf * D::kStageBytes;
+        const int c = 2 * s + hg;
 #pragma unroll
-  for (int s = 0; s < DSTAGES - 1; ++s) issue(min(s, nk - 1), s);
-  GMOE_WAIT_VM_LGKM0(2 * D::Q);  // stage 0 has landed
-  lds_barrier();
-  read_frags(0, 0, fw[0], fx[0]);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & (DSTAGES - 1);
-    // buffer (kt+3) mod 4 was last read in stage kt-1, released by its barrier
-    issue(min(kt + DSTAGES - 1, nk - 1), (kt + DSTAGES - 1) & (DSTAGES - 1));
-    read_frags(buf, 1, fw[1], fx[1]);
-    mfma_step(0);
-    // order: step-1 fragment reads first (their latency hides under the
-    // step-0 MFMAs), then the MFMAs with the stage loads spread between them
-    // order: two step-0 MFMAs, then the step-1 fragment reads each followed
-    // by an MFMA, then the stage loads spread over the remaining MFMAs
-    constexpr int kMf = C::TI * C::TJ;
-    constexpr int kRd = C::TI + C::TJ;
-    constexpr int kHead = kMf >= kRd + 2 ? 2 : 0;
-    constexpr int kRest = kMf - kHead - kRd > 0 ? kMf - kHead - kRd : 0;
-    constexpr int kPair = D::Q < kRest ? D::Q : kRest;
-    if constexpr (kHead > 0) __builtin_amdgcn_sched_group_barrier(0x008, kHead, 0);
+        for (int i = 0; i < C::TI; ++i) {
+          const int R = BM + wtile_row<BM, GATEUP, NW>(wn, i) + r32;
+          wa[i] = *reinterpret_cast<const u32x4*>(b + R * D::ROWB + dslot<SB>(R, c) * 16);
+        }
 #pragma unroll
-    for (int q = 0; q < kRd; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (q < kMf - kHead) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
+        for (int j = 0; j < TJV; ++j) {
+          const int R = wm * C::RW + j * 32 + r32;
+          xa[j] = *reinterpret_cast<const u32x4*>(b + R * D::ROWB + dslot<SB>(R, c) * 16);
+        }
+      }
+    };
+    auto mfma_step = [&](int b) {
 #pragma unroll
-    for (int q = 0; q < kPair; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-    if constexpr (kRest > kPair) __builtin_amdgcn_sched_group_barrier(0x008, kRest - kPair, 0);
-    if constexpr (D::Q > kPair) __builtin_amdgcn_sched_group_barrier(0x020, D::Q - kPair, 0);
-    // the step-0 MFMAs stay above the wait, so the MFMA pipe is busy while
-    // the step-1 fragment reads complete
-    __builtin_amdgcn_sched_barrier(0);
-    // stage kt+1 has landed (at most stages kt+2, kt+3 in flight) and every
-    // read of this buffer is complete
-    GMOE_WAIT_VM_LGKM0(2 * D::Q);
+      for (int i = 0; i < C::TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJV; ++j) acc[i][j] = mfma32(fw[b][i], fx[b][j], acc[i][j]);
+    };
+    constexpr int kMf = C::TI * TJV;               // MFMAs per step
+    constexpr int kRd = TJV > 0 ? C::TI + TJV : 0;  // fragment reads per step
+
+    // prologue: stages 0..NS-2 in flight (indices past the end re-read the
+    // last stage, in bounds, into buffers nobody reads)
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) issue(min(s, nk - 1), s);
+    GMOE_WAIT_VM_LGKM0((NS - 2) * D::Q);  // stage 0 has landed
     lds_barrier();
-    read_frags((kt + 1) & (DSTAGES - 1), 0, fw[0], fx[0]);
-    mfma_step(1);
-    __builtin_amdgcn_sched_group_barrier(0x100, C::TI + C::TJ, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, kMf, 0);
+    frags(0, 0, fw[0], fx[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt % NS;
+      // buffer (kt+NS-1) mod NS was last read in stage kt-1, released by its barrier
+      issue(min(kt + NS - 1, nk - 1), (kt + NS - 1) % NS);
+#pragma unroll
+      for (int s = 0; s + 1 < D::STEPS; ++s) {
+        frags(buf, s + 1, fw[(s + 1) & 1], fx[(s + 1) & 1]);
+        mfma_step(s & 1);
+      }
+      // order in the region above: the next step's fragment reads each paired
+      // with an MFMA, the stage loads spread over the remaining MFMAs
+      constexpr int kM = kMf * (D::STEPS - 1), kR = kRd * (D::STEPS - 1);
+      constexpr int kRP = kR < kM ? kR : kM;
+      constexpr int kGP = D::Q < kM - kRP ? D::Q : kM - kRP;
+#pragma unroll
+      for (int q = 0; q < kRP; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < kGP; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      if constexpr (kM > kRP + kGP) __builtin_amdgcn_sched_group_barrier(0x008, kM - kRP - kGP, 0);
+      if constexpr (kR > kRP) __builtin_amdgcn_sched_group_barrier(0x100, kR - kRP, 0);
+      if constexpr (D::Q > kGP) __builtin_amdgcn_sched_group_barrier(0x020, D::Q - kGP, 0);
+      // the MFMAs above stay above the wait, so the MFMA pipe is busy while
+      // the last fragment reads of the stage complete
+      __builtin_amdgcn_sched_barrier(0);
+      // stage kt+1 has landed (at most NS-2 later stages in flight) and every
+      // read of this buffer is complete
+      GMOE_WAIT_VM_LGKM0((NS - 2) * D::Q);
+      lds_barrier();
+      frags((kt + 1) % NS, 0, fw[0], fx[0]);
+      mfma_step((D::STEPS - 1) & 1);
+      if constexpr (kRd > 0) __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
+      if constexpr (kMf > 0) __builtin_amdgcn_sched_group_barrier(0x008, kMf, 0);
+    }
+  };
+  const int valid_rows = t.M - wm * C::RW;
+  const int tjv = valid_rows <= 0 ? 0 : min(C::TJ, (valid_rows + 31) / 32);
+  if (tjv >= C::TJ) {
+    stage_loop(std::integral_constant<int, C::TJ>{});
+  } else if (tjv == 0) {
+    stage_loop(std::integral_constant<int, 0>{});
+  } else if (tjv == 1) {
+    stage_loop(std::integral_constant<int, 1>{});
+  } else if constexpr (C::TJ > 2) {
+    if (tjv == 2)
+      stage_loop(std::integral_constant<int, 2>{});
+    else
+      stage_loop(std::integral_constant<int, (C::TJ > 3 ? 3 : 2)>{});
   }
   // drain the (duplicate) loads still in flight before the workgroup exits
   GMOE_WAIT_VM_LGKM0(0);
@@ -474,19 +515,27 @@ static hipError_t launch_staged(hipStream_t st, const bf16_bits* A, RouteView rv
   return hipGetLastError();
 }
 
+// Pipeline shape per tile height: 256-row tiles run 8 wavefronts (two per
+// SIMD, so one's MFMAs cover the other's waits).
+template <int BM>
+struct DmaChoice {
+  static constexpr int NW = BM == 256 ? 8 : 4;
+  static constexpr int SB = GMOE_DMA_SB;
+  static constexpr int NS = SB == 64 ? (BM == 256 ? 2 : 3) : 4;
+};
+
 template <int BM, bool GATEUP>
 static hipError_t launch_dma(hipStream_t st, const bf16_bits* A, RouteView rv, const void* w0, const void* w1,
                              int64_t T, int64_t rows_cap, int K, int N, int E, int Ftot, void* out) {
-  // 256-row tiles run 8 wavefronts (two per SIMD, so one's MFMAs cover the
-  // other's waits); smaller tiles run 4
-  constexpr int NW = BM == 256 ? 8 : 4;
-  constexpr int lds = DmaCfg<BM, NW>::kLdsBytes;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&dma_kernel<BM, GATEUP, NW>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  using P = DmaChoice<BM>;
+  constexpr int lds = DmaCfg<BM, P::NW, P::SB, P::NS>::kLdsBytes;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&dma_kernel<BM, GATEUP, P::NW, P::SB, P::NS>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   const dim3 grid(tiled_blocks(BM, rows_cap, E, N / (GATEUP ? TBN / 2 : TBN)));
-  hipLaunchKernelGGL((dma_kernel<BM, GATEUP, NW>), grid, dim3(NW * 64), lds, st, A, rv, w0, w1, T, K, N, E, Ftot,
-                     out);
+  hipLaunchKernelGGL((dma_kernel<BM, GATEUP, P::NW, P::SB, P::NS>), grid, dim3(P::NW * 64), lds, st, A, rv, w0, w1,
+                     T, K, N, E, Ftot, out);
   return hipGetLastError();
 }
 
