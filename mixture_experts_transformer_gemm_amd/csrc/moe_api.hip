@@ -9,11 +9,12 @@ using namespace gmoe;
 
 namespace {
 
-enum Path { PATH_F32 = 0, PATH_SKINNY = 1, PATH_TILED = 2 };
+enum Path { PATH_F32 = 0, PATH_SKINNY = 1, PATH_TILED = 2, PATH_STREAM = 3 };
 
 constexpr int64_t kMaxT = int64_t(1) << 20;
 constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int kSkinnyMaxT = 64;
+constexpr int kStreamMaxT = 16;
 
 struct Plan {
   int path = 0;
@@ -41,11 +42,17 @@ int check_shape(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t a
   return GROK_MOE_OK;
 }
 
-Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t act) {
+Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t act, int32_t wdt) {
   Plan p;
   p.rows_cap = T * k;
   if (act == GROK_MOE_F32) {
     p.path = PATH_F32;
+  } else if (T <= kStreamMaxT && wdt == GROK_MOE_BF16) {
+    p.path = PATH_STREAM;
+    p.mt_max = (int)T;  // rows of one expert <= T
+    int s = 1;
+    while (s < 8 && (int64_t)E * (d / 64) * s < 2048 && (f / (2 * s)) % 64 == 0) s *= 2;
+    p.splits = s;
   } else if (T <= kSkinnyMaxT) {
     p.path = PATH_SKINNY;
     const int64_t sub = (T + 15) / 16;  // rows of one expert <= T
@@ -115,7 +122,7 @@ extern "C" {
 size_t grok_moe_workspace_bytes(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t act_dtype,
                                 int32_t w_dtype) {
   if (check_shape(T, d, f, E, k, act_dtype, w_dtype) != GROK_MOE_OK) return 0;
-  return make_plan(T, d, f, E, k, act_dtype).total;
+  return make_plan(T, d, f, E, k, act_dtype, w_dtype).total;
 }
 
 int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const grok_moe_debug* dbg,
@@ -123,7 +130,7 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
   int rc = validate(a);
   if (rc != GROK_MOE_OK) return rc;
   if (a->T == 0) return GROK_MOE_OK;
-  const Plan p = make_plan(a->T, a->d, a->f, a->E, a->k, a->act_dtype);
+  const Plan p = make_plan(a->T, a->d, a->f, a->E, a->k, a->act_dtype, a->w_dtype);
   if (!ws || ws_bytes < p.total) return GROK_MOE_EWORKSPACE;
   if (((uintptr_t)ws & 255) != 0) return GROK_MOE_EALIGN;
 
@@ -162,6 +169,9 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
   if (p.path == PATH_F32) {
     GMOE_TRY(launch_f32_gateup((const float*)a->x, rv, (const float*)a->w_gate, (const float*)a->w_up, T,
                                p.rows_cap, d, f, E, (float*)H, st));
+  } else if (p.path == PATH_STREAM) {
+    GMOE_TRY(launch_stream_gateup(p.mt_max, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, T, d, f, E,
+                                  (bf16_bits*)H, st));
   } else if (p.path == PATH_SKINNY) {
     GMOE_TRY(launch_skinny_gateup(w8, p.mt_max, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, a->scales, T, d,
                                   f, E, (bf16_bits*)H, st));
@@ -173,6 +183,9 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
   if (!record(dbg, 3, st)) return GROK_MOE_EHIP;
   if (p.path == PATH_F32) {
     GMOE_TRY(launch_f32_down((const float*)H, rv, (const float*)a->w_down, p.rows_cap, d, f, E, Y, st));
+  } else if (p.path == PATH_STREAM) {
+    GMOE_TRY(launch_stream_down(p.mt_max, p.splits, (const bf16_bits*)H, rv, a->w_down, p.rows_cap, d, f, E, Y,
+                                st));
   } else if (p.path == PATH_SKINNY) {
     GMOE_TRY(launch_skinny_down(w8, p.mt_max, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales,
                                 p.rows_cap, d, f, E, Y, st));
