@@ -27,6 +27,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
+METRIC = "MoE-layer tokens/s + % roofline (HBM GB/s @T\u226464, MFMA util @T=8192)"
+
 WORKLOAD_NAMES = {
     "decode": "grok1_moe_layer_decode_T8",
     "prefill": "grok1_moe_layer_prefill_T8192",
@@ -46,8 +48,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="override the token count T (decode-shape sweep over T <= 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens the oracle times (0 = default per workload)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="the oracle repeats its sample until this much wall time has passed")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the FETCH/WRITE_SIZE counters)")
     return ap.parse_args()
@@ -88,9 +94,12 @@ def main():
 
     name = args.workload
     t0 = time.perf_counter()
-    w = synthetic.make(name)
+    w = synthetic.make(name, T=args.tokens or None)
     log(f"generated {name} (T={w.T} d={w.d} f={w.f} E={w.E} k={w.k} weights {w.w_dtype}) in "
         f"{time.perf_counter() - t0:.1f}s")
+    workload = WORKLOAD_NAMES[name]
+    if args.tokens:
+        workload = f"{workload.rsplit('_T', 1)[0]}_T{w.T}"
 
     def dev(a):
         if a is None:
@@ -121,20 +130,18 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # timed region: exactly K steps, no per-stage events
+    # Timed region: exactly K steps. The library records a HIP event before and
+    # after each stage on the launch stream (asynchronous, no host sync), which
+    # gives every kernel's duration over the same steps.
+    ev = HipEvents(6 * args.steps)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for s in range(args.steps):
+        step(events=ev.handles[6 * s:6 * s + 6])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed / args.steps * 1e3
     tokens_per_s = w.T * args.steps / elapsed
-
-    # per-stage kernel durations: HIP events recorded by the library on the launch stream
-    ev = HipEvents(6 * args.steps)
-    for s in range(args.steps):
-        step(events=ev.handles[6 * s:6 * s + 6])
-    torch.cuda.synchronize()
     stage_ms = {n: 0.0 for n in gm.STAGES}
     for s in range(args.steps):
         for i, n in enumerate(gm.STAGES):
@@ -142,7 +149,9 @@ def main():
     ev.close()
     log("stage ms: " + ", ".join(f"{n}={v:.4f}" for n, v in stage_ms.items()))
 
-    # algorithmic work of the dominant kernel (gate/up grouped GEMM + GELU*up)
+    # algorithmic work of the dominant kernel (gate/up grouped GEMM + GELU*up):
+    # per hit expert its two d x f weight matrices, plus the routed rows of x
+    # read and the H rows written; 4*d*f FLOPs per routed row
     wbytes = 1 if w.w_dtype == "i8" else (4 if w.w_dtype == "f32" else 2)
     abytes = 4 if w.act_dtype == "f32" else 2
     gu_bytes = n_hit * 2 * w.d * w.f * wbytes + rows * w.d * abytes + rows * w.f * abytes
@@ -152,7 +161,7 @@ def main():
     layer_bytes = (n_hit * 3 * w.d * w.f * wbytes + 2 * w.T * w.d * abytes + w.E * w.d * abytes)
     layer_flops = 6.0 * rows * w.d * w.f + 2.0 * w.T * w.d * w.E
     gu_s = stage_ms["gate_up"] / 1e3
-    hbm_bound = name in ("decode", "int8") or gu_flops / gu_bytes < (MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS) * 1e3
+    hbm_bound = gu_flops / gu_bytes < (MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS) * 1e3
     if hbm_bound:
         achieved = gu_bytes / gu_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -161,26 +170,17 @@ def main():
         achieved = gu_flops / gu_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
-    roof.update({"kernel": "gate_up grouped GEMM (+GELU*up)", "algorithmic_per_launch":
-                 gu_bytes if hbm_bound else gu_flops, "avg_launch_ms": round(stage_ms["gate_up"], 5),
-                 "traffic": None})
+    roof["traffic"], traffic_note = measured_traffic(workload)
+    roof.update({"kernel": "gate_up grouped GEMM (+GELU*up)",
+                 "algorithmic_per_launch": gu_bytes if hbm_bound else gu_flops,
+                 "avg_launch_ms": round(stage_ms["gate_up"], 5), "traffic_source": traffic_note})
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        n = args.cpu_sample or {"decode": 8, "tiny_f32": 64, "int8": 8, "skew": 8, "prefill": 8}[name]
-        n = min(n, w.T)
-        cores = oracle.threads()
-        log(f"timing the CPU oracle on {n} tokens with {cores} threads")
-        t0 = time.perf_counter()
-        oracle.forward(w.x[:n], w.router_w, w.w_gate, w.w_up, w.w_down, w.k, scales=w.scales, nthreads=cores)
-        dt = time.perf_counter() - t0
-        cpu = {"value": round(n / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-               "sample": f"first {n} of the {w.T} tokens, whole layer (routing, {w.k} experts each, combine), "
-                         f"fp64, {dt:.2f}s"}
+        cpu = cpu_baseline(w, name, args)
 
     result = {
-        "metric": "MoE-layer tokens/s + % roofline (HBM GB/s @T<=64, MFMA util @T=8192)",
+        "metric": METRIC,
         "value": round(tokens_per_s, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -192,7 +192,7 @@ def main():
         "vs_baseline": None,
         "dtype": {"bf16": "bf16", "i8": "int8w-bf16", "f32": "f32"}[w.w_dtype],
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[name], "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k,
+        "config": {"workload": workload, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k,
                    "weights": w.w_dtype, "experts_hit": n_hit},
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -201,6 +201,57 @@ def main():
                   "stage_ms": {k2: round(v, 5) for k2, v in stage_ms.items()}},
     }
     print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, name, args):
+    """Times the CPU oracle on the host cores over a bounded sample of the same
+    batch: the first n tokens, whole layer, repeated until about
+    ``--cpu-seconds`` of wall time has passed."""
+    import oracle
+    n = args.cpu_sample or {"tiny_f32": 64}.get(name, 8)
+    n = min(n, w.T)
+    cores = oracle.threads()
+    log(f"timing the CPU oracle on {n} tokens with {cores} threads (about {args.cpu_seconds:.0f} s)")
+    passes, dt = 0, 0.0
+    t0 = time.perf_counter()
+    while passes == 0 or (dt < args.cpu_seconds and passes < 100000):
+        oracle.forward(w.x[:n], w.router_w, w.w_gate, w.w_up, w.w_down, w.k, scales=w.scales, nthreads=cores)
+        passes += 1
+        dt = time.perf_counter() - t0
+    return {"value": round(n * passes / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of the {w.T} tokens, {passes} pass(es), whole layer (routing, {w.k} experts "
+                      f"per token, combine) in fp64: {dt:.2f} s"}
+
+
+def _source_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for fn in files:
+        with open(os.path.join(ROOT, "mixture_experts_transformer_gemm_amd", "csrc", fn), "rb") as fh:
+            h.update(fn.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, each scaled by the factor a
+    plain device copy of known size gives. None when no summary covers the
+    workload or the kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    for line in open(path):
+        if not line.startswith("workload="):
+            continue
+        kv = dict(item.split("=", 1) for item in line.split())
+        if kv["workload"] != workload:
+            continue
+        if _source_digest(kv["sources"].split(",")) != kv["sha256"]:
+            return None, "kernel sources changed since the counters were taken"
+        traffic = (float(kv["fetch_kib"]) * float(kv["fetch_factor"]) +
+                   float(kv["write_kib"]) * float(kv["write_factor"])) * 1024.0
+        return round(traffic), "profiles/hbm_traffic.txt"
+    return None, "no counter summary for this workload"
 
 
 if __name__ == "__main__":

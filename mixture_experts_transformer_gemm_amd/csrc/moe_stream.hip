@@ -115,14 +115,24 @@ __global__ __launch_bounds__(256) void stream_kernel(const bf16_bits* __restrict
 
   const int r16 = lane & 15, g = lane >> 4;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  // prologue: stages 0..kNS-2 in flight (past the end: re-read the last stage)
+  // prologue: stages 0..kNS-2 in flight (no load past the last stage: every
+  // weight byte is fetched once)
 #pragma unroll
-  for (int s = 0; s < kNS - 1; ++s) issue(min(s, nk - 1), s);
+  for (int s = 0; s < kNS - 1; ++s)
+    if (s < nk) issue(s, s);
   for (int kt = 0; kt < nk; ++kt) {
-    GMOE_WAIT_VM((kNS - 2) * Q);  // stage kt has landed in the ring
+    // stage kt has landed in the ring: the loads of the stages after it
+    // (min(nk - 1 - kt, kNS - 2) of them) may still be in flight
+    switch (min(nk - 1 - kt, kNS - 2)) {
+      case 4: GMOE_WAIT_VM(4 * Q); break;
+      case 3: GMOE_WAIT_VM(3 * Q); break;
+      case 2: GMOE_WAIT_VM(2 * Q); break;
+      case 1: GMOE_WAIT_VM(1 * Q); break;
+      default: GMOE_WAIT_VM(0); break;
+    }
     __asm__ __volatile__("" ::: "memory");  // no LDS access moves above the wait
     // the slot of stage kt-1 was fully read (its MFMAs consumed it): refill it
-    issue(min(kt + kNS - 1, nk - 1), (kt + kNS - 1) % kNS);
+    if (kt + kNS - 1 < nk) issue(kt + kNS - 1, (kt + kNS - 1) % kNS);
     const char* b = ring + (kt % kNS) * kStageB;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
