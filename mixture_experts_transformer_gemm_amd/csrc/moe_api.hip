@@ -14,7 +14,7 @@ enum Path { PATH_F32 = 0, PATH_SKINNY = 1, PATH_TILED = 2, PATH_STREAM = 3 };
 constexpr int64_t kMaxT = int64_t(1) << 20;
 constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int kSkinnyMaxT = 64;
-constexpr int kStreamMaxT = 16;
+constexpr int kStreamMaxT = 64;
 
 struct Plan {
   int path = 0;

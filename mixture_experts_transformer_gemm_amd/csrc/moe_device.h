@@ -80,4 +80,13 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                  0, 0, 0);
 }
 
+// Workgroup barrier without the vmcnt(0) a __syncthreads() fence implies (the
+// caller waits for exactly the loads it needs). The empty asm statements with
+// a memory clobber stop the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
 }  // namespace gmoe

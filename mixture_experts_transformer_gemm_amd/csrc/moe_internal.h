@@ -58,7 +58,7 @@ hipError_t launch_skinny_down(int w8, int mt_max, int splits, const bf16_bits* H
                               const float* scales, int64_t rows_cap, int d, int f, int E, float* Y,
                               hipStream_t stream);
 
-// Decode path (bf16 weights, every expert segment <= max_rows <= 16 rows).
+// Decode path (bf16 weights, every expert segment <= max_rows <= 64 rows).
 hipError_t launch_stream_gateup(int max_rows, const bf16_bits* x, RouteView rv, const void* wg, const void* wu,
                                 int64_t T, int d, int f, int E, bf16_bits* H, hipStream_t stream);
 hipError_t launch_stream_down(int max_rows, int splits, const bf16_bits* H, RouteView rv, const void* wd,

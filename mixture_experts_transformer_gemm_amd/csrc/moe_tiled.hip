@@ -41,7 +41,19 @@ constexpr int TBN = 256;
 #ifndef GMOE_DMA_SB
 #define GMOE_DMA_SB 64
 #endif
-constexpr int kGroupM = 8;
+#ifndef GMOE_PHASED
+#define GMOE_PHASED 1
+#endif
+#ifndef GMOE_ISSUE_STEP
+#define GMOE_ISSUE_STEP 0
+#endif
+#ifndef GMOE_PERSIST
+#define GMOE_PERSIST 0
+#endif
+#ifndef GMOE_GROUPM
+#define GMOE_GROUPM 8
+#endif
+constexpr int kGroupM = GMOE_GROUPM;
 
 template <int BM, int NW = 4>
 struct TileCfg {
@@ -64,14 +76,14 @@ using AccT = f32x16[TileCfg<BM, NW>::TI][TileCfg<BM, NW>::TJ];
 // Balanced per-XCD ranges over the tiles that exist; false when this
 // workgroup has no tile.
 template <int BM, bool GATEUP>
-__device__ __forceinline__ bool select_tile(const RouteView& rv, int E, int N, Tile& t) {
+__device__ __forceinline__ bool select_tile(const RouteView& rv, int E, int N, Tile& t, int slot) {
   constexpr int kTileCh = GATEUP ? TBN / 2 : TBN;  // output channels per tile
   const int nN = N / kTileCh;
   int mtiles = 0;
   for (int q = 0; q < E; ++q) mtiles += (rv.counts[q] + BM - 1) / BM;
   const int total = mtiles * nN;
   const int per_xcd = (total + 7) >> 3;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int xcd = blockIdx.x & 7;
   if (slot >= per_xcd) return false;
   const int L = xcd * per_xcd + slot;
   if (L >= total) return false;
@@ -239,15 +251,6 @@ __device__ __forceinline__ void dma16(const void* src, char* lds_base) {
 // s_waitcnt with vmcnt(n) and lgkmcnt(0) (expcnt left at its maximum)
 #define GMOE_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (((n) >> 4) << 14))
 
-// Workgroup barrier without the vmcnt(0) a __syncthreads() fence implies (the
-// caller waits for exactly the loads it needs). The empty asm statements with
-// a memory clobber stop the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  __asm__ __volatile__("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ __volatile__("" ::: "memory");
-}
-
 template <int BM, bool GATEUP, int NW, int SB, int NS>
 __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __restrict__ A, RouteView rv,
                                                      const void* __restrict__ w0, const void* __restrict__ w1,
@@ -256,8 +259,14 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
   using C = TileCfg<BM, NW>;
   using D = DmaCfg<BM, NW, SB, NS>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
+  // Persistent form: the grid holds as many workgroups as fit on the chip
+  // at once, and each walks the tiles of its XCD's range in steps of the
+  // XCD's workgroup count, so the workgroups of one XCD move through their
+  // tiles together and share operand stages in its L2.
+  const int slot_step = GMOE_PERSIST ? (int)(gridDim.x >> 3) : 0;
+  for (int slot = blockIdx.x >> 3;; slot += slot_step) {
   Tile t;
-  if (!select_tile<BM, GATEUP>(rv, E, N, t)) return;
+  if (!select_tile<BM, GATEUP>(rv, E, N, t, slot)) return;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hg = lane >> 5;
@@ -323,6 +332,32 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
     GMOE_WAIT_VM_LGKM0((NS - 2) * D::Q);  // stage 0 has landed
     lds_barrier();
     frags(0, 0, fw[0], fx[0]);
+#if GMOE_PHASED
+    // Each step is one phase: the fragment reads of the next step, then the
+    // MFMAs of this step (which use the fragments read one phase earlier).
+    // Scheduling fences keep the phases apart, so no MFMA waits on a read
+    // issued in its own phase.
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt % NS;
+#pragma unroll
+      for (int s = 0; s + 1 < D::STEPS; ++s) {
+        frags(buf, s + 1, fw[(s + 1) & 1], fx[(s + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(s & 1);
+        // buffer (kt+NS-1) mod NS was last read in stage kt-1, released by its barrier
+        if (s == GMOE_ISSUE_STEP) issue(min(kt + NS - 1, nk - 1), (kt + NS - 1) % NS);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // stage kt+1 has landed (at most NS-2 later stages in flight) and every
+      // read of this buffer is complete
+      GMOE_WAIT_VM_LGKM0((NS - 2) * D::Q);
+      lds_barrier();
+      frags((kt + 1) % NS, 0, fw[0], fx[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step((D::STEPS - 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#else
     for (int kt = 0; kt < nk; ++kt) {
       const int buf = kt % NS;
       // buffer (kt+NS-1) mod NS was last read in stage kt-1, released by its barrier
@@ -362,6 +397,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
       if constexpr (kRd > 0) __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
       if constexpr (kMf > 0) __builtin_amdgcn_sched_group_barrier(0x008, kMf, 0);
     }
+#endif
   };
   const int valid_rows = t.M - wm * C::RW;
   const int tjv = valid_rows <= 0 ? 0 : min(C::TJ, (valid_rows + 31) / 32);
@@ -380,6 +416,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
   // drain the (duplicate) loads still in flight before the workgroup exits
   GMOE_WAIT_VM_LGKM0(0);
   epilogue<BM, GATEUP, false, NW>(acc, t, nullptr, N, E, Ftot, out);
+  if (!GMOE_PERSIST) return;
+  // every wavefront is done with the LDS stages before the next tile's loads
+  lds_barrier();
+  }
 }
 
 // =====================================================================
@@ -409,7 +449,7 @@ __global__ __launch_bounds__(256, 1) void staged_kernel(const bf16_bits* __restr
   using S = StagedCfg<BM>;
   extern __shared__ __attribute__((aligned(16))) bf16_bits smem[];
   Tile t;
-  if (!select_tile<BM, GATEUP>(rv, E, N, t)) return;
+  if (!select_tile<BM, GATEUP>(rv, E, N, t, blockIdx.x >> 3)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, hg = lane >> 5;
@@ -519,9 +559,15 @@ static hipError_t launch_staged(hipStream_t st, const bf16_bits* A, RouteView rv
 // SIMD, so one's MFMAs cover the other's waits).
 template <int BM>
 struct DmaChoice {
-  static constexpr int NW = BM == 256 ? 8 : 4;
-  static constexpr int SB = GMOE_DMA_SB;
-  static constexpr int NS = SB == 64 ? (BM == 256 ? 2 : 3) : 4;
+#ifndef GMOE_NW256
+#define GMOE_NW256 8
+#endif
+#ifndef GMOE_DMA_NS256
+#define GMOE_DMA_NS256 2
+#endif
+  static constexpr int NW = BM == 256 ? GMOE_NW256 : 4;
+  static constexpr int SB = BM == 256 ? GMOE_DMA_SB : 64;
+  static constexpr int NS = BM == 256 ? GMOE_DMA_NS256 : 3;
 };
 
 template <int BM, bool GATEUP>
@@ -533,7 +579,18 @@ static hipError_t launch_dma(hipStream_t st, const bf16_bits* A, RouteView rv, c
       hipFuncSetAttribute(reinterpret_cast<const void*>(&dma_kernel<BM, GATEUP, P::NW, P::SB, P::NS>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  const dim3 grid(tiled_blocks(BM, rows_cap, E, N / (GATEUP ? TBN / 2 : TBN)));
+  unsigned blocks = tiled_blocks(BM, rows_cap, E, N / (GATEUP ? TBN / 2 : TBN));
+  if (GMOE_PERSIST) {
+    static const unsigned resident = [] {
+      int dev = 0, cus = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+      return (unsigned)(cus + 7) / 8 * 8;  // one workgroup per CU (LDS-bound)
+    }();
+    blocks = blocks < resident ? blocks : resident;
+  }
+  const dim3 grid(blocks);
   hipLaunchKernelGGL((dma_kernel<BM, GATEUP, P::NW, P::SB, P::NS>), grid, dim3(P::NW * 64), lds, st, A, rv, w0, w1,
                      T, K, N, E, Ftot, out);
   return hipGetLastError();
