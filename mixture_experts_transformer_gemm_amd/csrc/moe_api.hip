@@ -65,6 +65,18 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ac
     p.path = PATH_TILED;
     // about k*T/E rows per expert: the tile height that wastes little of it
     p.bm = T <= 384 ? 64 : (T <= 1536 ? 128 : 256);
+#ifndef GMOE_W8_BM
+#define GMOE_W8_BM 128
+#endif
+    // 8-bit weights: one row tile per expert up to 128 rows, so each weight
+    // tile is streamed from HBM once
+    if (wdt == GROK_MOE_I8 && T <= 1536) p.bm = GMOE_W8_BM;
+    // split the down projection's reduction while its tiles alone would
+    // leave CUs idle: (row tiles upper bound) x (d / 256) tiles per split
+    const int64_t tiles = (p.rows_cap / p.bm + E) * (d / 256);
+    int s = 1;
+    while (s < 8 && tiles * s < 1024 && (f / (2 * s)) % 64 == 0) s *= 2;
+    p.splits = s;
   }
   const size_t hsz = act == GROK_MOE_F32 ? 4 : 2;
   size_t o = 0;
@@ -190,7 +202,8 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
     GMOE_TRY(launch_skinny_down(w8, p.mt_max, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales,
                                 p.rows_cap, d, f, E, Y, st));
   } else {
-    GMOE_TRY(launch_tiled_down(w8, p.bm, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d, f, E, Y, st));
+    GMOE_TRY(launch_tiled_down(w8, p.bm, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d, f,
+                               E, Y, st));
   }
   // stage 4: gate-weighted combine
   if (!record(dbg, 4, st)) return GROK_MOE_EHIP;

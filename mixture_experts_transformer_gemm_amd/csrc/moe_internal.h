@@ -69,8 +69,10 @@ hipError_t launch_stream_down(int max_rows, int splits, const bf16_bits* H, Rout
 hipError_t launch_tiled_gateup(int w8, int bm, const bf16_bits* x, RouteView rv, const void* wg, const void* wu,
                                const float* scales, int64_t T, int64_t rows_cap, int d, int f, int E,
                                bf16_bits* H, hipStream_t stream);
-hipError_t launch_tiled_down(int w8, int bm, const bf16_bits* H, RouteView rv, const void* wd, const float* scales,
-                             int64_t rows_cap, int d, int f, int E, float* Y, hipStream_t stream);
+// splits: partial sums over equal slices of the reduction (Y holds `splits` of them).
+hipError_t launch_tiled_down(int w8, int bm, int splits, const bf16_bits* H, RouteView rv, const void* wd,
+                             const float* scales, int64_t rows_cap, int d, int f, int E, float* Y,
+                             hipStream_t stream);
 
 // fp32 path (plain FMA kernels, fp32 accumulation).
 hipError_t launch_f32_gateup(const float* x, RouteView rv, const float* wg, const float* wu, int64_t T,

@@ -38,22 +38,7 @@ namespace gmoe {
 
 constexpr int TBN = 256;
 
-#ifndef GMOE_DMA_SB
-#define GMOE_DMA_SB 64
-#endif
-#ifndef GMOE_PHASED
-#define GMOE_PHASED 1
-#endif
-#ifndef GMOE_ISSUE_STEP
-#define GMOE_ISSUE_STEP 0
-#endif
-#ifndef GMOE_PERSIST
-#define GMOE_PERSIST 0
-#endif
-#ifndef GMOE_GROUPM
-#define GMOE_GROUPM 8
-#endif
-constexpr int kGroupM = GMOE_GROUPM;
+constexpr int kGroupM = 4;  // row tiles per tile group (see select_tile)
 
 template <int BM, int NW = 4>
 struct TileCfg {
@@ -206,13 +191,13 @@ __device__ __forceinline__ void zero_acc(AccT<BM, NW>& acc) {
 }
 
 // =====================================================================
-// bf16 weights: LDS filled by global_load_lds_dwordx4.
+// LDS filled by global_load_lds_dwordx4 (both weight types).
 //
-// A stage holds SB reduction values of every tile row: SB = 32 gives 64-byte
-// LDS rows (4 chunks of 16 bytes), SB = 64 gives 128-byte rows (8 chunks),
-// i.e. whole 128-byte lines of each global row per stage. NS LDS stages;
-// the loads of stage k+NS-1 are issued at the start of stage k. One
-// wavefront load instruction fills 1 KB of LDS: lane i writes row
+// A stage holds SB = 64 reduction values of every tile row: activation rows
+// of 128 bytes (bf16), weight rows of 128 bytes (bf16) or 64 bytes (8-bit,
+// kept as int8 in LDS and widened to bf16 after the fragment read, which is
+// exact). NS LDS stages; the loads of stage k+NS-1 are issued during stage
+// k. One wavefront load instruction fills 1 KB of LDS: lane i writes row
 // (1024 / row bytes) t + i / chunks, slot i mod chunks, so it fetches the
 // chunk that belongs in that slot.
 //
@@ -220,22 +205,34 @@ __device__ __forceinline__ void zero_acc(AccT<BM, NW>& acc) {
 // clocks): 64-byte rows put chunk c of row R at c ^ ((R >> 2) & 3); 128-byte
 // rows at c ^ (R & 7) ^ ((R >> 3) & 1). Both keep the fragment reads (lane
 // l: row l mod 32, chunk c + l / 32) free of bank conflicts.
+//
+// 8-bit weights: one 16-byte read gives a lane the 16 reduction values of
+// two MFMA steps. Lane half h (= l / 32) of the 32-value block d reads
+// values [32d + 16h, 32d + 16h + 16); the low 8 feed step 2d and the high 8
+// step 2d + 1, and the activation fragment of step 2d + e for lane half h is
+// read from the same reduction indices, [32d + 16h + 8e, +8). Each MFMA thus
+// pairs equal indices; only the order of the sum over the block differs.
 // =====================================================================
-template <int BM, int NW, int SB, int NS>
+template <int BM, int NW, int NS, bool W8>
 struct DmaCfg {
-  static constexpr int RT = BM + TBN;          // LDS rows per stage (activations, then weights)
-  static constexpr int ROWB = SB * 2;          // bytes per LDS row
-  static constexpr int CH = ROWB / 16;         // 16-byte chunks per row
-  static constexpr int RPI = 1024 / ROWB;      // rows per load instruction
-  static constexpr int Q = RT / (RPI * NW);    // load instructions per wavefront per stage
-  static constexpr int STEPS = SB / 16;        // MFMA steps per stage
-  static constexpr int kStageBytes = RT * ROWB;
+  static constexpr int SB = 64;                       // reduction values per stage
+  static constexpr int AROWB = SB * 2;                // activation bytes per LDS row
+  static constexpr int WROWB = W8 ? SB : SB * 2;      // weight bytes per LDS row
+  static constexpr int ACH = AROWB / 16, WCH = WROWB / 16;
+  static constexpr int ARPI = 1024 / AROWB, WRPI = 1024 / WROWB;  // rows per load instruction
+  static constexpr int QA = BM / (ARPI * NW);         // activation loads per wavefront per stage
+  static constexpr int QW = TBN / (WRPI * NW);        // weight loads per wavefront per stage
+  static constexpr int Q = QA + QW;
+  static constexpr int STEPS = SB / 16;               // MFMA steps per stage
+  static constexpr int kActBytes = BM * AROWB;
+  static constexpr int kStageBytes = kActBytes + TBN * WROWB;
   static constexpr int kLdsBytes = NS * kStageBytes;
+  static_assert(QA * ARPI * NW == BM && QW * WRPI * NW == TBN, "load shape");
 };
 
-template <int SB>
+template <int ROWB>
 __device__ __forceinline__ int dslot(int R, int c) {
-  if (SB == 32) return c ^ ((R >> 2) & 3);
+  if (ROWB == 64) return c ^ ((R >> 2) & 3);
   return c ^ (R & 7) ^ ((R >> 3) & 1);
 }
 
@@ -251,47 +248,73 @@ __device__ __forceinline__ void dma16(const void* src, char* lds_base) {
 // s_waitcnt with vmcnt(n) and lgkmcnt(0) (expcnt left at its maximum)
 #define GMOE_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (((n) >> 4) << 14))
 
-template <int BM, bool GATEUP, int NW, int SB, int NS>
+template <int BM, bool GATEUP, int NW, int NS, bool W8>
 __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __restrict__ A, RouteView rv,
                                                      const void* __restrict__ w0, const void* __restrict__ w1,
-                                                     int64_t T, int K, int N, int E, int Ftot,
-                                                     void* __restrict__ out) {
+                                                     const float* __restrict__ scales, int64_t T, int K, int N,
+                                                     int E, int Ftot, int64_t rows_cap, void* __restrict__ out) {
   using C = TileCfg<BM, NW>;
-  using D = DmaCfg<BM, NW, SB, NS>;
+  using D = DmaCfg<BM, NW, NS, W8>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  // Persistent form: the grid holds as many workgroups as fit on the chip
-  // at once, and each walks the tiles of its XCD's range in steps of the
-  // XCD's workgroup count, so the workgroups of one XCD move through their
-  // tiles together and share operand stages in its L2.
-  const int slot_step = GMOE_PERSIST ? (int)(gridDim.x >> 3) : 0;
-  for (int slot = blockIdx.x >> 3;; slot += slot_step) {
   Tile t;
-  if (!select_tile<BM, GATEUP>(rv, E, N, t, slot)) return;
+  if (!select_tile<BM, GATEUP>(rv, E, N, t, blockIdx.x >> 3)) return;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hg = lane >> 5;
   const int wn = wave % C::WN, wm = wave / C::WN;
+  // split-K (down pass only): this workgroup reduces [kbeg, kbeg + K / S)
+  // into partial sum sp
+  const int S = gridDim.y, sp = blockIdx.y;
+  const int kbeg = sp * (K / S);
+  if (!GATEUP) out = (float*)out + (int64_t)sp * rows_cap * N;
 
-  // source of each of this lane's Q load instructions (stage 0)
+  // source of each of this lane's load instructions (stage 0): QA activation
+  // instructions, then QW weight instructions. Activation instruction q holds
+  // tile rows [q ARPI NW, (q + 1) ARPI NW); those wholly past the segment's
+  // end are not issued (qav of them are).
+  const int qav = min(D::QA, (t.M + D::ARPI * NW - 1) / (D::ARPI * NW));
   const char* src[D::Q];
 #pragma unroll
-  for (int q = 0; q < D::Q; ++q) {
-    const int R = D::RPI * (q * NW + wave) + lane / D::CH;
-    const int c = dslot<SB>(R, lane % D::CH);
-    const char* row = R < BM ? (const char*)act_row<GATEUP>(A, rv, t, T, K, R)
-                             : weight_row<GATEUP>(w0, w1, t, N, K, 2, R - BM);
-    src[q] = row + c * 16;
+  for (int q = 0; q < D::QA; ++q) {
+    const int R = D::ARPI * (q * NW + wave) + lane / D::ACH;
+    const int c = dslot<D::AROWB>(R, lane % D::ACH);
+    src[q] = (const char*)(act_row<GATEUP>(A, rv, t, T, K, R) + kbeg) + c * 16;
   }
-  auto issue = [&](int stage, int buf) {
+#pragma unroll
+  for (int q = 0; q < D::QW; ++q) {
+    const int R = D::WRPI * (q * NW + wave) + lane / D::WCH;
+    const int c = dslot<D::WROWB>(R, lane % D::WCH);
+    src[D::QA + q] = weight_row<GATEUP>(w0, w1, t, N, K, W8 ? 1 : 2, R) + (size_t)kbeg * (W8 ? 1 : 2) + c * 16;
+  }
+  auto issue_act = [&](int stage, int buf) {
     char* dst = lds + buf * D::kStageBytes;
 #pragma unroll
-    for (int q = 0; q < D::Q; ++q) dma16(src[q] + (size_t)stage * D::ROWB, dst + (q * NW + wave) * 1024);
+    for (int q = 0; q < D::QA; ++q)
+      if (q < qav) dma16(src[q] + (size_t)stage * D::AROWB, dst + (q * NW + wave) * 1024);
   };
+  auto issue_w = [&](int stage, int buf) {
+    char* dst = lds + buf * D::kStageBytes;
+#pragma unroll
+    for (int q = 0; q < D::QW; ++q)
+      dma16(src[D::QA + q] + (size_t)stage * D::WROWB, dst + D::kActBytes + (q * NW + wave) * 1024);
+  };
+  // stage k has landed when at most NS-2 later stages of this wavefront's
+  // loads (qav + QW instructions each) are in flight; lgkmcnt(0) as well
+  auto wait_stage = [&]() {
+    switch (qav) {
+      case 1: GMOE_WAIT_VM_LGKM0((NS - 2) * (D::QW + 1)); break;
+      case 2: GMOE_WAIT_VM_LGKM0((NS - 2) * (D::QW + 2)); break;
+      case 3: GMOE_WAIT_VM_LGKM0((NS - 2) * (D::QW + 3)); break;
+      default: GMOE_WAIT_VM_LGKM0((NS - 2) * (D::QW + 4)); break;
+    }
+  };
+  static_assert(D::QA <= 4, "wait_stage covers up to 4 activation loads per stage");
 
   f32x16 acc[C::TI][C::TJ];
   zero_acc<BM, NW>(acc);
   u32x4 fw[2][C::TI], fx[2][C::TJ];
-  const int nk = K / SB;
+  u32x4 fhi[C::TI];  // 8-bit weights: the widened fragment of the next (odd) step
+  const int nk = K / S / D::SB;
 
   // The stage loop, for a wavefront whose first TJV row subtiles (of 32 rows)
   // hold rows of the segment: the others are past its end and get neither
@@ -303,16 +326,31 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
     auto frags = [&](int buf, int s, u32x4* wa, u32x4* xa) {
       if constexpr (TJV > 0) {
         const char* b = lds + buf * D::kStageBytes;
-        const int c = 2 * s + hg;
+        if (!W8) {
+          const int c = 2 * s + hg;
 #pragma unroll
-        for (int i = 0; i < C::TI; ++i) {
-          const int R = BM + wtile_row<BM, GATEUP, NW>(wn, i) + r32;
-          wa[i] = *reinterpret_cast<const u32x4*>(b + R * D::ROWB + dslot<SB>(R, c) * 16);
+          for (int i = 0; i < C::TI; ++i) {
+            const int R = wtile_row<BM, GATEUP, NW>(wn, i) + r32;
+            wa[i] = *reinterpret_cast<const u32x4*>(b + D::kActBytes + R * D::WROWB + dslot<D::WROWB>(R, c) * 16);
+          }
+        } else if ((s & 1) == 0) {
+          const int c = s + hg;  // block d = s / 2, chunk 2d + h
+#pragma unroll
+          for (int i = 0; i < C::TI; ++i) {
+            const int R = wtile_row<BM, GATEUP, NW>(wn, i) + r32;
+            const u32x4 q =
+                *reinterpret_cast<const u32x4*>(b + D::kActBytes + R * D::WROWB + dslot<D::WROWB>(R, c) * 16);
+            i8x16_to_frags(q, wa[i], fhi[i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < C::TI; ++i) wa[i] = fhi[i];
         }
+        const int cx = W8 ? (2 * (s & ~1) + 2 * hg + (s & 1)) : (2 * s + hg);
 #pragma unroll
         for (int j = 0; j < TJV; ++j) {
           const int R = wm * C::RW + j * 32 + r32;
-          xa[j] = *reinterpret_cast<const u32x4*>(b + R * D::ROWB + dslot<SB>(R, c) * 16);
+          xa[j] = *reinterpret_cast<const u32x4*>(b + R * D::AROWB + dslot<D::AROWB>(R, cx) * 16);
         }
       }
     };
@@ -322,17 +360,21 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
 #pragma unroll
         for (int j = 0; j < TJV; ++j) acc[i][j] = mfma32(fw[b][i], fx[b][j], acc[i][j]);
     };
-    constexpr int kMf = C::TI * TJV;               // MFMAs per step
-    constexpr int kRd = TJV > 0 ? C::TI + TJV : 0;  // fragment reads per step
 
     // prologue: stages 0..NS-2 in flight (indices past the end re-read the
     // last stage, in bounds, into buffers nobody reads)
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s) issue(min(s, nk - 1), s);
-    GMOE_WAIT_VM_LGKM0((NS - 2) * D::Q);  // stage 0 has landed
+    for (int s = 0; s < NS - 1; ++s) {
+      issue_act(min(s, nk - 1), s);
+      issue_w(min(s, nk - 1), s);
+    }
+    wait_stage();  // stage 0 has landed
     lds_barrier();
+    // Activation loads of a stage are issued right after the barrier that
+    // frees their buffer (outside the MFMA phases: whether each is issued
+    // depends on the segment), the weight loads inside the first phase.
+    issue_act(min(NS - 1, nk - 1), (NS - 1) % NS);
     frags(0, 0, fw[0], fx[0]);
-#if GMOE_PHASED
     // Each step is one phase: the fragment reads of the next step, then the
     // MFMAs of this step (which use the fragments read one phase earlier).
     // Scheduling fences keep the phases apart, so no MFMA waits on a read
@@ -345,59 +387,19 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(s & 1);
         // buffer (kt+NS-1) mod NS was last read in stage kt-1, released by its barrier
-        if (s == GMOE_ISSUE_STEP) issue(min(kt + NS - 1, nk - 1), (kt + NS - 1) % NS);
+        if (s == 0) issue_w(min(kt + NS - 1, nk - 1), (kt + NS - 1) % NS);
         __builtin_amdgcn_sched_barrier(0);
       }
       // stage kt+1 has landed (at most NS-2 later stages in flight) and every
       // read of this buffer is complete
-      GMOE_WAIT_VM_LGKM0((NS - 2) * D::Q);
+      wait_stage();
       lds_barrier();
+      issue_act(min(kt + NS, nk - 1), (kt + NS) % NS);
       frags((kt + 1) % NS, 0, fw[0], fx[0]);
       __builtin_amdgcn_sched_barrier(0);
       mfma_step((D::STEPS - 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-#else
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt % NS;
-      // buffer (kt+NS-1) mod NS was last read in stage kt-1, released by its barrier
-      issue(min(kt + NS - 1, nk - 1), (kt + NS - 1) % NS);
-#pragma unroll
-      for (int s = 0; s + 1 < D::STEPS; ++s) {
-        frags(buf, s + 1, fw[(s + 1) & 1], fx[(s + 1) & 1]);
-        mfma_step(s & 1);
-      }
-      // order in the region above: the next step's fragment reads each paired
-      // with an MFMA, the stage loads spread over the remaining MFMAs
-      constexpr int kM = kMf * (D::STEPS - 1), kR = kRd * (D::STEPS - 1);
-      constexpr int kRP = kR < kM ? kR : kM;
-      constexpr int kGP = D::Q < kM - kRP ? D::Q : kM - kRP;
-#pragma unroll
-      for (int q = 0; q < kRP; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-#pragma unroll
-      for (int q = 0; q < kGP; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
-      if constexpr (kM > kRP + kGP) __builtin_amdgcn_sched_group_barrier(0x008, kM - kRP - kGP, 0);
-      if constexpr (kR > kRP) __builtin_amdgcn_sched_group_barrier(0x100, kR - kRP, 0);
-      if constexpr (D::Q > kGP) __builtin_amdgcn_sched_group_barrier(0x020, D::Q - kGP, 0);
-      // the MFMAs above stay above the wait, so the MFMA pipe is busy while
-      // the last fragment reads of the stage complete
-      __builtin_amdgcn_sched_barrier(0);
-      // stage kt+1 has landed (at most NS-2 later stages in flight) and every
-      // read of this buffer is complete
-      GMOE_WAIT_VM_LGKM0((NS - 2) * D::Q);
-      lds_barrier();
-      frags((kt + 1) % NS, 0, fw[0], fx[0]);
-      mfma_step((D::STEPS - 1) & 1);
-      if constexpr (kRd > 0) __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
-      if constexpr (kMf > 0) __builtin_amdgcn_sched_group_barrier(0x008, kMf, 0);
-    }
-#endif
   };
   const int valid_rows = t.M - wm * C::RW;
   const int tjv = valid_rows <= 0 ? 0 : min(C::TJ, (valid_rows + 31) / 32);
@@ -415,120 +417,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
   }
   // drain the (duplicate) loads still in flight before the workgroup exits
   GMOE_WAIT_VM_LGKM0(0);
-  epilogue<BM, GATEUP, false, NW>(acc, t, nullptr, N, E, Ftot, out);
-  if (!GMOE_PERSIST) return;
-  // every wavefront is done with the LDS stages before the next tile's loads
-  lds_barrier();
-  }
-}
-
-// =====================================================================
-// 8-bit weights: 64-wide stages through registers (int8 -> bf16 on the way
-// into LDS). LDS rows hold 64 bf16 = 8 chunks of 16 bytes; chunk c of row r
-// sits at slot c ^ (r mod 8) ^ (bit 3 of r), so the rows read by 8 or by 16
-// consecutive lanes hit distinct bank groups.
-// =====================================================================
-constexpr int SBK = 64;
-
-__device__ __forceinline__ int swz(int r, int c) { return (r * 8 + (c ^ (r & 7) ^ ((r >> 3) & 1))) * 8; }
-
-template <int BM>
-struct StagedCfg {
-  static constexpr int AL = BM / 32;                // 16-byte activation chunks per thread per stage
-  static constexpr int WL = 4;                      // 16-byte int8 weight chunks per thread per stage
-  static constexpr int kStage = (BM + TBN) * SBK;   // bf16 elements per LDS stage
-  static constexpr int kLdsBytes = 2 * kStage * 2;
-};
-
-template <int BM, bool GATEUP>
-__global__ __launch_bounds__(256, 1) void staged_kernel(const bf16_bits* __restrict__ A, RouteView rv,
-                                                        const void* __restrict__ w0, const void* __restrict__ w1,
-                                                        const float* __restrict__ scales, int64_t T, int K, int N,
-                                                        int E, int Ftot, void* __restrict__ out) {
-  using C = TileCfg<BM>;
-  using S = StagedCfg<BM>;
-  extern __shared__ __attribute__((aligned(16))) bf16_bits smem[];
-  Tile t;
-  if (!select_tile<BM, GATEUP>(rv, E, N, t, blockIdx.x >> 3)) return;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r32 = lane & 31, hg = lane >> 5;
-  const int wn = wave % C::WN, wm = wave / C::WN;
-
-  // activation rows: chunk lc of rows lr + 32p; weight rows: 16-byte chunk qc
-  // of rows qr + 64p
-  const int lc = tid & 7, lr = tid >> 3;
-  const int qc = tid & 3, qr = tid >> 2;
-  const bf16_bits* arow[S::AL];
-#pragma unroll
-  for (int p = 0; p < S::AL; ++p) arow[p] = act_row<GATEUP>(A, rv, t, T, K, lr + 32 * p);
-  const char* wrow[S::WL];
-#pragma unroll
-  for (int p = 0; p < S::WL; ++p) wrow[p] = weight_row<GATEUP>(w0, w1, t, N, K, 1, qr + 64 * p);
-
-  u32x4 ra[S::AL], rw[S::WL];
-  auto gload = [&](int kb) {
-#pragma unroll
-    for (int p = 0; p < S::AL; ++p) ra[p] = ld16(arow[p] + kb + lc * 8);
-#pragma unroll
-    for (int p = 0; p < S::WL; ++p) rw[p] = ld16(wrow[p] + kb + qc * 16);
-  };
-  auto lstore = [&](int stage) {
-    bf16_bits* sa = smem + stage * S::kStage;
-    bf16_bits* sw = sa + BM * SBK;
-#pragma unroll
-    for (int p = 0; p < S::AL; ++p) *reinterpret_cast<u32x4*>(&sa[swz(lr + 32 * p, lc)]) = ra[p];
-#pragma unroll
-    for (int p = 0; p < S::WL; ++p) {
-      u32x4 lo, hi;
-      i8x16_to_frags(rw[p], lo, hi);
-      const int r = qr + 64 * p;
-      *reinterpret_cast<u32x4*>(&sw[swz(r, 2 * qc)]) = lo;
-      *reinterpret_cast<u32x4*>(&sw[swz(r, 2 * qc + 1)]) = hi;
-    }
-  };
-  auto read_frags = [&](int stage, int s, u32x4* wa, u32x4* xa) {
-    const bf16_bits* sa = smem + stage * S::kStage;
-    const bf16_bits* sw = sa + BM * SBK;
-    const int c = 2 * s + hg;
-#pragma unroll
-    for (int i = 0; i < C::TI; ++i)
-      wa[i] = *reinterpret_cast<const u32x4*>(&sw[swz(wtile_row<BM, GATEUP>(wn, i) + r32, c)]);
-#pragma unroll
-    for (int j = 0; j < C::TJ; ++j)
-      xa[j] = *reinterpret_cast<const u32x4*>(&sa[swz(wm * C::RW + j * 32 + r32, c)]);
-  };
-
-  f32x16 acc[C::TI][C::TJ];
-  zero_acc<BM>(acc);
-  u32x4 fw[2][C::TI], fx[2][C::TJ];
-  const int nk = K / SBK;
-  gload(0);
-  lstore(0);
-  gload(min(1, nk - 1) * SBK);
-  __syncthreads();
-  read_frags(0, 0, fw[0], fx[0]);
-  // one basic block per stage: past the end the prefetch re-reads the last
-  // stage (in bounds) and the store goes to the buffer nobody reads
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    lstore(cur ^ 1);
-    // keep the new loads behind the stores, so the stores wait for the loads
-    // issued a stage ago and not for these
-    __builtin_amdgcn_sched_barrier(0);
-    gload(min(kt + 2, nk - 1) * SBK);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s < 3) read_frags(cur, s + 1, fw[(s + 1) & 1], fx[(s + 1) & 1]);
-#pragma unroll
-      for (int i = 0; i < C::TI; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TJ; ++j) acc[i][j] = mfma32(fw[s & 1][i], fx[s & 1][j], acc[i][j]);
-    }
-    __syncthreads();
-    read_frags(cur ^ 1, 0, fw[0], fx[0]);
-  }
-  epilogue<BM, GATEUP, true>(acc, t, scales, N, E, Ftot, out);
+  epilogue<BM, GATEUP, W8, NW>(acc, t, scales, N, E, Ftot, out);
 }
 
 // =====================================================================
@@ -541,77 +430,50 @@ static unsigned tiled_blocks(int bm, int64_t rows_cap, int E, int nN) {
   return (unsigned)(((mt_ub * nN) + 7) / 8 * 8);
 }
 
-template <int BM, bool GATEUP>
-static hipError_t launch_staged(hipStream_t st, const bf16_bits* A, RouteView rv, const void* w0, const void* w1,
-                                const float* scales, int64_t T, int64_t rows_cap, int K, int N, int E, int Ftot,
-                                void* out) {
-  constexpr int lds = StagedCfg<BM>::kLdsBytes;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&staged_kernel<BM, GATEUP>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (attr != hipSuccess) return attr;
-  const dim3 grid(tiled_blocks(BM, rows_cap, E, N / (GATEUP ? TBN / 2 : TBN)));
-  hipLaunchKernelGGL((staged_kernel<BM, GATEUP>), grid, dim3(256), lds, st, A, rv, w0, w1, scales, T, K, N, E,
-                     Ftot, out);
-  return hipGetLastError();
-}
-
 // Pipeline shape per tile height: 256-row tiles run 8 wavefronts (two per
-// SIMD, so one's MFMAs cover the other's waits).
-template <int BM>
+// SIMD, so one's MFMAs cover the other's waits); as many LDS stages as fit
+// in 144 KB, at most 6.
+template <int BM, bool W8>
 struct DmaChoice {
-#ifndef GMOE_NW256
-#define GMOE_NW256 8
-#endif
-#ifndef GMOE_DMA_NS256
-#define GMOE_DMA_NS256 2
-#endif
-  static constexpr int NW = BM == 256 ? GMOE_NW256 : 4;
-  static constexpr int SB = BM == 256 ? GMOE_DMA_SB : 64;
-  static constexpr int NS = BM == 256 ? GMOE_DMA_NS256 : 3;
+  static constexpr int NW = BM == 256 ? 8 : 4;
+  static constexpr int kStage = DmaCfg<BM, NW, 2, W8>::kStageBytes;
+  static constexpr int NS = 147456 / kStage < 6 ? 147456 / kStage : 6;
 };
 
-template <int BM, bool GATEUP>
+template <int BM, bool GATEUP, bool W8>
 static hipError_t launch_dma(hipStream_t st, const bf16_bits* A, RouteView rv, const void* w0, const void* w1,
-                             int64_t T, int64_t rows_cap, int K, int N, int E, int Ftot, void* out) {
-  using P = DmaChoice<BM>;
-  constexpr int lds = DmaCfg<BM, P::NW, P::SB, P::NS>::kLdsBytes;
+                             const float* scales, int64_t T, int64_t rows_cap, int K, int N, int E, int Ftot,
+                             int splits, void* out) {
+  using P = DmaChoice<BM, W8>;
+  constexpr int lds = DmaCfg<BM, P::NW, P::NS, W8>::kLdsBytes;
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&dma_kernel<BM, GATEUP, P::NW, P::SB, P::NS>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&dma_kernel<BM, GATEUP, P::NW, P::NS, W8>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  unsigned blocks = tiled_blocks(BM, rows_cap, E, N / (GATEUP ? TBN / 2 : TBN));
-  if (GMOE_PERSIST) {
-    static const unsigned resident = [] {
-      int dev = 0, cus = 0;
-      if (hipGetDevice(&dev) != hipSuccess ||
-          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
-      return (unsigned)(cus + 7) / 8 * 8;  // one workgroup per CU (LDS-bound)
-    }();
-    blocks = blocks < resident ? blocks : resident;
-  }
-  const dim3 grid(blocks);
-  hipLaunchKernelGGL((dma_kernel<BM, GATEUP, P::NW, P::SB, P::NS>), grid, dim3(P::NW * 64), lds, st, A, rv, w0, w1,
-                     T, K, N, E, Ftot, out);
+  const dim3 grid(tiled_blocks(BM, rows_cap, E, N / (GATEUP ? TBN / 2 : TBN)), (unsigned)splits);
+  hipLaunchKernelGGL((dma_kernel<BM, GATEUP, P::NW, P::NS, W8>), grid, dim3(P::NW * 64), lds, st, A, rv, w0, w1,
+                     scales, T, K, N, E, Ftot, rows_cap, out);
   return hipGetLastError();
 }
 
 template <int BM, bool GATEUP>
 static hipError_t tiled_launch(bool w8, hipStream_t st, const bf16_bits* A, RouteView rv, const void* w0,
                                const void* w1, const float* scales, int64_t T, int64_t rows_cap, int K, int N, int E,
-                               int Ftot, void* out) {
-  return w8 ? launch_staged<BM, GATEUP>(st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, out)
-            : launch_dma<BM, GATEUP>(st, A, rv, w0, w1, T, rows_cap, K, N, E, Ftot, out);
+                               int Ftot, int splits, void* out) {
+  return w8 ? launch_dma<BM, GATEUP, true>(st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, out)
+            : launch_dma<BM, GATEUP, false>(st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, out);
 }
 
 template <bool GATEUP>
 static hipError_t tiled_dispatch(bool w8, int bm, hipStream_t st, const bf16_bits* A, RouteView rv, const void* w0,
                                  const void* w1, const float* scales, int64_t T, int64_t rows_cap, int K, int N,
-                                 int E, int Ftot, void* out) {
+                                 int E, int Ftot, int splits, void* out) {
   switch (bm) {
-    case 64: return tiled_launch<64, GATEUP>(w8, st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, out);
-    case 128: return tiled_launch<128, GATEUP>(w8, st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, out);
-    case 256: return tiled_launch<256, GATEUP>(w8, st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, out);
+    case 64: return tiled_launch<64, GATEUP>(w8, st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, out);
+    case 128:
+      return tiled_launch<128, GATEUP>(w8, st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, out);
+    case 256:
+      return tiled_launch<256, GATEUP>(w8, st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, out);
   }
   return hipErrorInvalidValue;
 }
@@ -619,12 +481,12 @@ static hipError_t tiled_dispatch(bool w8, int bm, hipStream_t st, const bf16_bit
 hipError_t launch_tiled_gateup(int w8, int bm, const bf16_bits* x, RouteView rv, const void* wg, const void* wu,
                                const float* scales, int64_t T, int64_t rows_cap, int d, int f, int E,
                                bf16_bits* H, hipStream_t st) {
-  return tiled_dispatch<true>(w8 != 0, bm, st, x, rv, wg, wu, scales, T, rows_cap, d, f, E, f, H);
+  return tiled_dispatch<true>(w8 != 0, bm, st, x, rv, wg, wu, scales, T, rows_cap, d, f, E, f, 1, H);
 }
 
-hipError_t launch_tiled_down(int w8, int bm, const bf16_bits* H, RouteView rv, const void* wd, const float* scales,
-                             int64_t rows_cap, int d, int f, int E, float* Y, hipStream_t st) {
-  return tiled_dispatch<false>(w8 != 0, bm, st, H, rv, wd, wd, scales, rows_cap, rows_cap, f, d, E, f, Y);
+hipError_t launch_tiled_down(int w8, int bm, int splits, const bf16_bits* H, RouteView rv, const void* wd,
+                             const float* scales, int64_t rows_cap, int d, int f, int E, float* Y, hipStream_t st) {
+  return tiled_dispatch<false>(w8 != 0, bm, st, H, rv, wd, wd, scales, rows_cap, rows_cap, f, d, E, f, splits, Y);
 }
 
 }  // namespace gmoe

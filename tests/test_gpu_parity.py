@@ -51,7 +51,7 @@ def test_bf16_layer_other_shapes(T, d, f):
     _full_check(w)
 
 
-@pytest.mark.parametrize("T", [3, 40, 128, 200, 513])
+@pytest.mark.parametrize("T", [3, 40, 128, 200, 513, 1600])
 def test_int8_layer_small_random_scales(T):
     # distinct per-channel scales pin which output channel each scale belongs to
     w = synthetic.make("int8", T=T, d=256, f=512, seed=T)
