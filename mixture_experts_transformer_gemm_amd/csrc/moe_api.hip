@@ -9,11 +9,11 @@ using namespace gmoe;
 
 namespace {
 
-enum Path { PATH_F32 = 0, PATH_SKINNY = 1, PATH_TILED = 2, PATH_STREAM = 3 };
+enum Path { PATH_F32 = 0, PATH_STREAM8 = 1, PATH_TILED = 2, PATH_STREAM = 3 };
 
 constexpr int64_t kMaxT = int64_t(1) << 20;
 constexpr int64_t kMaxDim = int64_t(1) << 20;
-constexpr int kSkinnyMaxT = 64;
+constexpr int kStream8MaxT = 256;
 constexpr int kStreamMaxT = 64;
 
 struct Plan {
@@ -53,13 +53,12 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ac
     int s = 1;
     while (s < 8 && (int64_t)E * (d / 64) * s < 2048 && (f / (2 * s)) % 64 == 0) s *= 2;
     p.splits = s;
-  } else if (T <= kSkinnyMaxT) {
-    p.path = PATH_SKINNY;
-    const int64_t sub = (T + 15) / 16;  // rows of one expert <= T
-    p.mt_max = sub <= 1 ? 1 : sub <= 2 ? 2 : 4;
-    // enough workgroups for the down projection to keep every CU streaming
+  } else if (T <= kStream8MaxT && wdt == GROK_MOE_I8) {
+    p.path = PATH_STREAM8;
+    p.mt_max = (int)T;  // rows of one expert <= T
+    // enough workgroups (of 256 output channels) for the down projection
     int s = 1;
-    while (s < 8 && (int64_t)E * (d / 64) * s < 2048 && (f / (2 * s)) % 64 == 0) s *= 2;
+    while (s < 4 && (int64_t)E * (d / 256) * s < 1024 && (f / (2 * s)) % 64 == 0) s *= 2;
     p.splits = s;
   } else {
     p.path = PATH_TILED;
@@ -184,9 +183,9 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
   } else if (p.path == PATH_STREAM) {
     GMOE_TRY(launch_stream_gateup(p.mt_max, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, T, d, f, E,
                                   (bf16_bits*)H, st));
-  } else if (p.path == PATH_SKINNY) {
-    GMOE_TRY(launch_skinny_gateup(w8, p.mt_max, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, a->scales, T, d,
-                                  f, E, (bf16_bits*)H, st));
+  } else if (p.path == PATH_STREAM8) {
+    GMOE_TRY(launch_stream8_gateup(p.mt_max, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, a->scales, T, d, f, E,
+                                   (bf16_bits*)H, st));
   } else {
     GMOE_TRY(launch_tiled_gateup(w8, p.bm, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, a->scales, T, p.rows_cap, d,
                                  f, E, (bf16_bits*)H, st));
@@ -198,9 +197,9 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
   } else if (p.path == PATH_STREAM) {
     GMOE_TRY(launch_stream_down(p.mt_max, p.splits, (const bf16_bits*)H, rv, a->w_down, p.rows_cap, d, f, E, Y,
                                 st));
-  } else if (p.path == PATH_SKINNY) {
-    GMOE_TRY(launch_skinny_down(w8, p.mt_max, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales,
-                                p.rows_cap, d, f, E, Y, st));
+  } else if (p.path == PATH_STREAM8) {
+    GMOE_TRY(launch_stream8_down(p.mt_max, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d, f,
+                                 E, Y, st));
   } else {
     GMOE_TRY(launch_tiled_down(w8, p.bm, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d, f,
                                E, Y, st));

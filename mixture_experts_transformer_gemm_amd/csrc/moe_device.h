@@ -89,4 +89,23 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ __volatile__("" ::: "memory");
 }
 
+// 16 bytes per lane from global memory straight into LDS (global_load_lds):
+// lane i of the wavefront writes lds_base + 16 i (lds_base must be
+// wavefront-uniform). POLICY is the instruction's cache-policy field (0
+// default, 2 nontemporal). The builtin only exists in the device pass.
+template <int POLICY>
+__device__ __forceinline__ void dma16_policy(const void* src, char* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, POLICY);
+#endif
+}
+
+// slot of 16-byte chunk c of LDS row r for 128-byte rows (conflict-free for
+// fragment reads of 16 consecutive rows at one chunk, and of 32 rows at two
+// chunks, measured on gfx950)
+__device__ __forceinline__ int rslot(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+
+// s_waitcnt vmcnt(n), other counters left alone
+#define GMOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
 }  // namespace gmoe

@@ -42,19 +42,10 @@ namespace {
 constexpr int kSB = 64;      // reduction values per stage
 constexpr int kRowB = 128;   // LDS bytes per row and stage
 
-// slot of 16-byte chunk c of ring row r (conflict-free for the fragment reads)
-__device__ __forceinline__ int rslot(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
-
-// 16 bytes per lane straight into LDS (lane i writes lds_base + 16 i) with
-// the nontemporal cache policy: each weight byte is read exactly once, and
-// on MI355X the streaming reads reach about 7 TB/s only with this hint.
-__device__ __forceinline__ void dma16s(const void* src, char* lds_base) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, /*nt*/ 2);
-#endif
-}
-
-#define GMOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+// 16 bytes per lane straight into LDS with the nontemporal cache policy:
+// each weight byte is read exactly once, and on MI355X the streaming reads
+// reach about 7 TB/s only with this hint.
+__device__ __forceinline__ void dma16s(const void* src, char* lds_base) { dma16_policy<2>(src, lds_base); }
 
 }  // namespace
 
