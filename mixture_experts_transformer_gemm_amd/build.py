@@ -28,17 +28,37 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
+def scratch_kernels(remarks: str):
+    """Kernels whose resource-usage remark reports private (scratch) memory:
+    a register array the compiler could not keep in registers, which costs a
+    memory round trip per access in the hot loops."""
+    bad, name = [], None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:", 1)[1].split("[")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in line and name:
+            size = int(line.split("ScratchSize [bytes/lane]:", 1)[1].split("[")[0].strip())
+            if size:
+                bad.append((name, size))
+    return bad
+
+
 def build(verbose: bool = False) -> str:
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
     tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + inc + sources() + ["-o", tmp]
+    cmd = [HIPCC] + FLAGS + ["-Rpass-analysis=kernel-resource-usage"] + inc + sources() + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)
+    lines = (res.stderr or "").splitlines()
+    err = "\n".join(l for l in lines if noise not in l and "remark:" not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    bad = scratch_kernels(res.stderr or "")
+    if bad:
+        os.remove(tmp)
+        raise RuntimeError("kernels use scratch memory: " + ", ".join(f"{n} ({b} B/lane)" for n, b in bad))
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, LIB)

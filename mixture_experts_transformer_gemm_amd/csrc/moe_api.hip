@@ -9,7 +9,7 @@ using namespace gmoe;
 
 namespace {
 
-enum Path { PATH_F32 = 0, PATH_STREAM8 = 1, PATH_TILED = 2, PATH_STREAM = 3 };
+enum Path { PATH_F32 = 0, PATH_TILED = 2, PATH_STREAM = 3 };
 
 constexpr int64_t kMaxT = int64_t(1) << 20;
 constexpr int64_t kMaxDim = int64_t(1) << 20;
@@ -47,18 +47,14 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ac
   p.rows_cap = T * k;
   if (act == GROK_MOE_F32) {
     p.path = PATH_F32;
-  } else if (T <= kStreamMaxT && wdt == GROK_MOE_BF16) {
+  } else if ((wdt == GROK_MOE_BF16 && T <= kStreamMaxT) || (wdt == GROK_MOE_I8 && T <= kStream8MaxT)) {
     p.path = PATH_STREAM;
     p.mt_max = (int)T;  // rows of one expert <= T
+    // enough workgroups (of 128 output channels) for the down projection;
+    // each split keeps whole stages (64 bf16 or 128 8-bit reduction values)
+    const int64_t ks = wdt == GROK_MOE_I8 ? 128 : 64;
     int s = 1;
-    while (s < 8 && (int64_t)E * (d / 64) * s < 2048 && (f / (2 * s)) % 64 == 0) s *= 2;
-    p.splits = s;
-  } else if (T <= kStream8MaxT && wdt == GROK_MOE_I8) {
-    p.path = PATH_STREAM8;
-    p.mt_max = (int)T;  // rows of one expert <= T
-    // enough workgroups (of 256 output channels) for the down projection
-    int s = 1;
-    while (s < 4 && (int64_t)E * (d / 256) * s < 1024 && (f / (2 * s)) % 64 == 0) s *= 2;
+    while (s < 8 && (int64_t)E * (d / 64) * s < 2048 && (f / (2 * s)) % ks == 0) s *= 2;
     p.splits = s;
   } else {
     p.path = PATH_TILED;
@@ -181,11 +177,8 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
     GMOE_TRY(launch_f32_gateup((const float*)a->x, rv, (const float*)a->w_gate, (const float*)a->w_up, T,
                                p.rows_cap, d, f, E, (float*)H, st));
   } else if (p.path == PATH_STREAM) {
-    GMOE_TRY(launch_stream_gateup(p.mt_max, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, T, d, f, E,
-                                  (bf16_bits*)H, st));
-  } else if (p.path == PATH_STREAM8) {
-    GMOE_TRY(launch_stream8_gateup(p.mt_max, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, a->scales, T, d, f, E,
-                                   (bf16_bits*)H, st));
+    GMOE_TRY(launch_stream_gateup(w8, p.mt_max, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, a->scales, T, d, f,
+                                  E, (bf16_bits*)H, st));
   } else {
     GMOE_TRY(launch_tiled_gateup(w8, p.bm, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, a->scales, T, p.rows_cap, d,
                                  f, E, (bf16_bits*)H, st));
@@ -195,11 +188,8 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
   if (p.path == PATH_F32) {
     GMOE_TRY(launch_f32_down((const float*)H, rv, (const float*)a->w_down, p.rows_cap, d, f, E, Y, st));
   } else if (p.path == PATH_STREAM) {
-    GMOE_TRY(launch_stream_down(p.mt_max, p.splits, (const bf16_bits*)H, rv, a->w_down, p.rows_cap, d, f, E, Y,
-                                st));
-  } else if (p.path == PATH_STREAM8) {
-    GMOE_TRY(launch_stream8_down(p.mt_max, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d, f,
-                                 E, Y, st));
+    GMOE_TRY(launch_stream_down(w8, p.mt_max, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d,
+                                f, E, Y, st));
   } else {
     GMOE_TRY(launch_tiled_down(w8, p.bm, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d, f,
                                E, Y, st));

@@ -50,20 +50,15 @@ hipError_t launch_permute(const int32_t* idx, int64_t T, int E, int k, int32_t* 
 hipError_t launch_combine(int out_f32, const float* Y, int S, int64_t rows_cap, const int32_t* pos,
                           const float* gate, int64_t T, int d, int k, void* out, hipStream_t stream);
 
-// Decode path (bf16 weights, every expert segment <= max_rows <= 64 rows).
-hipError_t launch_stream_gateup(int max_rows, const bf16_bits* x, RouteView rv, const void* wg, const void* wu,
-                                int64_t T, int d, int f, int E, bf16_bits* H, hipStream_t stream);
-hipError_t launch_stream_down(int max_rows, int splits, const bf16_bits* H, RouteView rv, const void* wd,
-                              int64_t rows_cap, int d, int f, int E, float* Y, hipStream_t stream);
-
-// 8-bit weights, segments processed in chunks of up to 128 rows (weights
-// streamed into registers, activations shared through LDS).
-hipError_t launch_stream8_gateup(int max_rows, const bf16_bits* x, RouteView rv, const void* wg, const void* wu,
-                                 const float* scales, int64_t T, int d, int f, int E, bf16_bits* H,
-                                 hipStream_t stream);
-hipError_t launch_stream8_down(int max_rows, int splits, const bf16_bits* H, RouteView rv, const void* wd,
-                               const float* scales, int64_t rows_cap, int d, int f, int E, float* Y,
-                               hipStream_t stream);
+// Weight-streaming path: bf16 weights with every expert segment <= max_rows
+// <= 64 rows, or 8-bit weights (w8, scales) with segments processed in
+// chunks of up to 128 rows.
+hipError_t launch_stream_gateup(int w8, int max_rows, const bf16_bits* x, RouteView rv, const void* wg,
+                                const void* wu, const float* scales, int64_t T, int d, int f, int E, bf16_bits* H,
+                                hipStream_t stream);
+hipError_t launch_stream_down(int w8, int max_rows, int splits, const bf16_bits* H, RouteView rv, const void* wd,
+                              const float* scales, int64_t rows_cap, int d, int f, int E, float* Y,
+                              hipStream_t stream);
 
 // Large-M path (LDS-tiled MFMA grouped GEMM).
 // bm: rows per workgroup tile (64, 128 or 256).

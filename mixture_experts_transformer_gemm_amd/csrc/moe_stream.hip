@@ -49,17 +49,32 @@ __device__ __forceinline__ void dma16s(const void* src, char* lds_base) { dma16_
 
 }  // namespace
 
-// Segments of up to 16*MT rows (MT = 1, 2, 4).
+// Segments processed in chunks of up to 16*MT rows (MT = 1, 2, 4, 8; chunk
+// z of a segment along grid z). W8: 8-bit weights.
 constexpr int kBW = 8;               // wavefronts per workgroup
 constexpr int kBWRows = 16 * kBW;    // weight rows per workgroup stage
 
-template <int MT>
+// A stage holds kRowB bytes of every weight row: 64 reduction values of bf16
+// weights, 128 of 8-bit weights; activation rows (bf16) hold the same
+// reduction values: 128 or 256 bytes.
+template <int MT, bool W8>
 struct BsCfg {
-  static constexpr int XR = 16 * MT;                    // activation rows per stage
-  static constexpr int kStageB = (kBWRows + XR) * kRowB;
+  static constexpr int XR = 16 * MT;                     // activation rows per chunk
+  static constexpr int KS = W8 ? 128 : 64;               // reduction values per stage
+  static constexpr int AROWB = KS * 2;                   // activation bytes per row and stage
+  static constexpr int ARPI = 1024 / AROWB;              // activation rows per load instruction
+  static constexpr int NI = XR / ARPI;                   // activation load instructions per stage (max)
+  static constexpr int kQA = (NI + kBW - 1) / kBW;       // of which one wavefront issues at most
+  static constexpr int kActOff = kBWRows * kRowB;        // activation rows follow the weight rows
+  static constexpr int kStageB = kActOff + XR * AROWB;
+  // as many stages as fit in 144 KB, at most 8
   static constexpr int NS = 147456 / kStageB < 8 ? 147456 / kStageB : 8;
   static constexpr int kLdsBytes = NS * kStageB;
 };
+
+// slot of 16-byte chunk c of a 256-byte activation row r (16 chunks; the 16
+// rows read at one chunk land in 16 distinct bank groups)
+__device__ __forceinline__ int aslot256(int r, int c) { return c ^ (r & 15); }
 
 // s_waitcnt vmcnt(p * Q) for a run-time p in [0, 6]
 template <int Q>
@@ -76,13 +91,12 @@ __device__ __forceinline__ void wait_stages(int p) {
   __asm__ __volatile__("" ::: "memory");  // no LDS access moves above the wait
 }
 
-template <bool GATEUP, int MT>
+template <bool GATEUP, int MT, bool W8>
 __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __restrict__ A, RouteView rv,
-                                                          const bf16_bits* __restrict__ w0,
-                                                          const bf16_bits* __restrict__ w1, int64_t T, int K,
+                                                          const void* __restrict__ w0, const void* __restrict__ w1,
+                                                          const float* __restrict__ scales, int64_t T, int K,
                                                           int N, int E, int64_t rows_cap, void* __restrict__ out) {
-  using C = BsCfg<MT>;
-  constexpr int NS = C::NS;
+  using C = BsCfg<MT, W8>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -91,36 +105,41 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
   const int e = blockIdx.x / nblk;
   const int nb = blockIdx.x - e * nblk;
   const int M = rv.counts[e];
-  if (M <= 0) return;
-  const int m0 = rv.offsets[e];
+  const int mbase = (int)blockIdx.z * C::XR;  // first row of this chunk within the segment
+  if (mbase >= M) return;
+  const int m0 = rv.offsets[e] + mbase;
   const int c0 = nb * kBW * kChW + wave * kChW;
   const int S = gridDim.y, sp = blockIdx.y;
   const int kspan = K / S, kbeg = sp * kspan;
-  const int nk = kspan / kSB;
-  const int rows = min(M, C::XR);
-  const int na = (rows + 7) >> 3;   // activation load instructions per stage
-  const int mv = (rows + 15) >> 4;  // 16-row MFMA tiles with rows
+  const int nk = kspan / C::KS;
+  const int rows = min(M - mbase, C::XR);
+  const int na = (rows + C::ARPI - 1) / C::ARPI;  // activation load instructions per stage
+  const int mv = (rows + 15) >> 4;                // 16-row MFMA tiles with rows
+  constexpr size_t wsz = W8 ? 1 : 2;
 
   // this lane's sources: two weight instructions (rows 8q + lane / 8 of the
-  // wavefront's 16) and, for wavefronts below na, one activation instruction
+  // wavefront's 16) and the activation instructions wave, wave + 8, ... < na
   const char* wsrc[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int r = 8 * q + (lane >> 3);
     const int R = 16 * wave + r;  // ring row
     const int c = rslot(R, lane & 7);
-    const bf16_bits* row;
+    const char* row;
     if (GATEUP)
-      row = (r < 8 ? w0 : w1) + ((int64_t)e * N + c0 + (r & 7)) * K;
+      row = (const char*)(r < 8 ? w0 : w1) + ((int64_t)e * N + c0 + (r & 7)) * K * wsz;
     else
-      row = w0 + ((int64_t)e * N + c0 + r) * K;
-    wsrc[q] = (const char*)(row + kbeg) + c * 16;
+      row = (const char*)w0 + ((int64_t)e * N + c0 + r) * K * wsz;
+    wsrc[q] = row + kbeg * wsz + c * 16;
   }
-  const char* asrc = nullptr;
-  if (wave < na) {
-    int xr = 8 * wave + (lane >> 3);
-    const int c = rslot(kBWRows + xr, lane & 7);
-    if (xr >= M) xr = M - 1;
+  const char* asrc[C::kQA];
+#pragma unroll
+  for (int a = 0; a < C::kQA; ++a) {
+    const int inst = wave + kBW * a;
+    const int ar = C::ARPI * (inst < C::NI ? inst : 0) + lane / (C::AROWB / 16);  // activation row
+    const int ch = lane % (C::AROWB / 16);
+    const int c = W8 ? aslot256(ar, ch) : rslot(kBWRows + ar, ch);
+    const int xr = ar < rows ? ar : rows - 1;
     const bf16_bits* row;
     if (GATEUP) {
       int tok = rv.perm[m0 + xr];
@@ -129,27 +148,46 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
     } else {
       row = A + (int64_t)(m0 + xr) * K;
     }
-    asrc = (const char*)(row + kbeg) + c * 16;
+    asrc[a] = (const char*)(row + kbeg) + c * 16;
   }
+  // instructions this wavefront issues per stage (0 .. kQA)
+  const int naw = na > wave ? (na - wave + kBW - 1) / kBW : 0;
   // workgroups start their walk over the reduction at different stages, so
   // that concurrent workgroups spread over the HBM channels
-  const int rot = (int)(((unsigned)blockIdx.x * 37u + (unsigned)sp * 11u) % (unsigned)nk);
+  const int rot = (int)(((unsigned)blockIdx.x * 37u + (unsigned)sp * 11u + (unsigned)blockIdx.z * 5u) % (unsigned)nk);
 
   const int r16 = lane & 15, g = lane >> 4;
   f32x4 acc[MT];
 #pragma unroll
   for (int j = 0; j < MT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto run = [&](auto act_tag) {
-    constexpr bool HAS_ACT = decltype(act_tag)::value;
-    constexpr int Q = HAS_ACT ? 3 : 2;  // this wavefront's load instructions per stage
-    auto issue = [&](int stage, int slot) {
+  // MFMA step on tiles 0..MV-1: weight fragment wa, activation chunk cx
+  auto tiles = [&](const char* b, u32x4 wa, int cx, auto mv_tag) __attribute__((always_inline)) {
+    constexpr int MV = decltype(mv_tag)::value;
+    u32x4 xa[MV];
+#pragma unroll
+    for (int j = 0; j < MV; ++j) {
+      const int xr = 16 * j + r16;
+      const int slot = W8 ? aslot256(xr, cx) : rslot(kBWRows + xr, cx);
+      xa[j] = *reinterpret_cast<const u32x4*>(b + C::kActOff + xr * C::AROWB + slot * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < MV; ++j) acc[j] = mfma16(wa, xa[j], acc[j]);
+  };
+
+  auto run = [&](auto naw_tag, auto mv_tag) __attribute__((always_inline)) {
+    constexpr int NAW = decltype(naw_tag)::value;
+    constexpr int Q = 2 + NAW;  // this wavefront's load instructions per stage
+    constexpr int NS = C::NS;
+    auto issue = [&](int stage, int slot) __attribute__((always_inline)) {
       int ks = stage + rot;
       if (ks >= nk) ks -= nk;
       char* dst = lds + slot * C::kStageB;
       dma16s(wsrc[0] + (size_t)ks * kRowB, dst + (16 * wave) * kRowB);
       dma16s(wsrc[1] + (size_t)ks * kRowB, dst + (16 * wave + 8) * kRowB);
-      if (HAS_ACT) dma16s(asrc + (size_t)ks * kRowB, dst + (kBWRows + 8 * wave) * kRowB);
+#pragma unroll
+      for (int a = 0; a < NAW; ++a)
+        dma16s(asrc[a] + (size_t)ks * C::AROWB, dst + C::kActOff + (wave + kBW * a) * 1024);
     };
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
@@ -162,80 +200,134 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
       lds_barrier();
       if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
       const char* b = lds + (kt % NS) * C::kStageB;
+      const int wr = 16 * wave + r16;
+      if (!W8) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int c = 4 * s + g;
-        const int wr = 16 * wave + r16;
-        const u32x4 wa = *reinterpret_cast<const u32x4*>(b + wr * kRowB + rslot(wr, c) * 16);
+        for (int s = 0; s < 2; ++s) {
+          const int c = 4 * s + g;  // reduction values [32s + 8g, +8)
+          const u32x4 wa = *reinterpret_cast<const u32x4*>(b + wr * kRowB + rslot(wr, c) * 16);
+          tiles(b, wa, c, mv_tag);
+        }
+      } else {
+        // 8-bit weights: lane group g of half h reads values [64h + 16g, +16):
+        // the low 8 feed step (h, 0), the high 8 step (h, 1); the activation
+        // chunk of step (h, s) holds values [64h + 16g + 8s, +8)
 #pragma unroll
-        for (int j = 0; j < MT; ++j) {
-          if (j < mv) {
-            const int xr = kBWRows + 16 * j + r16;
-            const u32x4 xa = *reinterpret_cast<const u32x4*>(b + xr * kRowB + rslot(xr, c) * 16);
-            acc[j] = mfma16(wa, xa, acc[j]);
-          }
+        for (int h = 0; h < 2; ++h) {
+          const int c = 4 * h + g;
+          const u32x4 q = *reinterpret_cast<const u32x4*>(b + wr * kRowB + rslot(wr, c) * 16);
+          u32x4 lo, hi;
+          i8x16_to_frags(q, lo, hi);
+          tiles(b, lo, 8 * h + 2 * g, mv_tag);
+          tiles(b, hi, 8 * h + 2 * g + 1, mv_tag);
         }
       }
     }
   };
-  if (wave < na)
-    run(std::integral_constant<bool, true>{});
+  // MV: tiles that get MFMAs (the chunk's rows rounded up to MT/2 or MT
+  // tiles; rows past the segment's end repeat its last row)
+  constexpr int kHalf = MT > 1 ? MT / 2 : 1;
+  auto run_naw = [&](auto naw_tag) __attribute__((always_inline)) {
+    if (mv <= kHalf)
+      run(naw_tag, std::integral_constant<int, kHalf>{});
+    else
+      run(naw_tag, std::integral_constant<int, MT>{});
+  };
+  static_assert(C::kQA <= 4, "up to 4 activation loads per wavefront and stage");
+  if (naw >= 4 && C::kQA >= 4)
+    run_naw(std::integral_constant<int, (C::kQA >= 4 ? 4 : 0)>{});
+  else if (naw == 3 && C::kQA >= 3)
+    run_naw(std::integral_constant<int, (C::kQA >= 3 ? 3 : 0)>{});
+  else if (naw == 2 && C::kQA >= 2)
+    run_naw(std::integral_constant<int, (C::kQA >= 2 ? 2 : 0)>{});
+  else if (naw == 1)
+    run_naw(std::integral_constant<int, 1>{});
   else
-    run(std::integral_constant<bool, false>{});
+    run_naw(std::integral_constant<int, 0>{});
 
 #pragma unroll
   for (int j = 0; j < MT; ++j) {
     if (j < mv) {
-      const int m = 16 * j + r16;  // activation row of this lane's results
+      const int m = 16 * j + r16;  // activation row (within the chunk) of this lane's results
       if (GATEUP) {
         // lanes with g < 2 hold gate channels 4g..4g+3, lane + 32 the same up channels
         float up[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) up[v] = __shfl(acc[j][v], lane + 32, 64);
-        if (g < 2 && m < M) {
+        if (g < 2 && m < rows) {
           float h[4];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) h[v] = gelu_erf(acc[j][v]) * up[v];
+          for (int v = 0; v < 4; ++v) {
+            float gt = acc[j][v], u = up[v];
+            if (W8) {
+              gt *= scales[(int64_t)e * N + c0 + 4 * g + v];
+              u *= scales[(int64_t)E * N + (int64_t)e * N + c0 + 4 * g + v];
+            }
+            h[v] = gelu_erf(gt) * u;
+          }
           uint2 o;
           o.x = pack_bf16x2(h[0], h[1]);
           o.y = pack_bf16x2(h[2], h[3]);
           *reinterpret_cast<uint2*>((bf16_bits*)out + (int64_t)(m0 + m) * N + c0 + 4 * g) = o;
         }
-      } else if (m < M) {
+      } else if (m < rows) {
+        float y[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          y[v] = acc[j][v] * (W8 ? scales[2 * (int64_t)E * K + (int64_t)e * N + c0 + 4 * g + v] : 1.f);
         float* Ys = (float*)out + (int64_t)sp * rows_cap * N;
-        *reinterpret_cast<float4*>(Ys + (int64_t)(m0 + m) * N + c0 + 4 * g) =
-            make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+        *reinterpret_cast<float4*>(Ys + (int64_t)(m0 + m) * N + c0 + 4 * g) = make_float4(y[0], y[1], y[2], y[3]);
       }
     }
   }
 }
 
-template <bool GATEUP, int MT>
+template <bool GATEUP, int MT, bool W8>
 static hipError_t stream_launch(dim3 grid, hipStream_t st, const bf16_bits* A, RouteView rv, const void* w0,
-                                 const void* w1, int64_t T, int K, int N, int E, int64_t rows_cap, void* out) {
-  constexpr int lds = BsCfg<MT>::kLdsBytes;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&stream_kernel<GATEUP, MT>),
+                                const void* w1, const float* scales, int64_t T, int K, int N, int E,
+                                int64_t rows_cap, void* out) {
+  constexpr int lds = BsCfg<MT, W8>::kLdsBytes;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&stream_kernel<GATEUP, MT, W8>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((stream_kernel<GATEUP, MT>), grid, dim3(kBW * 64), lds, st, A, rv, (const bf16_bits*)w0,
-                     (const bf16_bits*)w1, T, K, N, E, rows_cap, out);
+  hipLaunchKernelGGL((stream_kernel<GATEUP, MT, W8>), grid, dim3(kBW * 64), lds, st, A, rv, w0, w1, scales, T, K,
+                     N, E, rows_cap, out);
   return hipGetLastError();
 }
 
-hipError_t launch_stream_gateup(int max_rows, const bf16_bits* x, RouteView rv, const void* wg, const void* wu,
-                                int64_t T, int d, int f, int E, bf16_bits* H, hipStream_t st) {
-  const dim3 grid((unsigned)E * (unsigned)(f / (kBW * 8)));
-  if (max_rows <= 16) return stream_launch<true, 1>(grid, st, x, rv, wg, wu, T, d, f, E, 0, H);
-  if (max_rows <= 32) return stream_launch<true, 2>(grid, st, x, rv, wg, wu, T, d, f, E, 0, H);
-  return stream_launch<true, 4>(grid, st, x, rv, wg, wu, T, d, f, E, 0, H);
+// rows of one expert <= max_rows; chunks of 16*MT rows along grid z
+template <bool GATEUP, bool W8>
+static hipError_t stream_dispatch(int max_rows, unsigned gx, unsigned gy, hipStream_t st, const bf16_bits* A,
+                                  RouteView rv, const void* w0, const void* w1, const float* scales, int64_t T,
+                                  int K, int N, int E, int64_t rows_cap, void* out) {
+  auto chunks = [&](int xr) { return (unsigned)((max_rows + xr - 1) / xr); };
+  if (max_rows <= 16)
+    return stream_launch<GATEUP, 1, W8>(dim3(gx, gy, 1), st, A, rv, w0, w1, scales, T, K, N, E, rows_cap, out);
+  if (max_rows <= 32)
+    return stream_launch<GATEUP, 2, W8>(dim3(gx, gy, 1), st, A, rv, w0, w1, scales, T, K, N, E, rows_cap, out);
+  if (max_rows <= 64 || !W8)
+    return stream_launch<GATEUP, 4, W8>(dim3(gx, gy, chunks(64)), st, A, rv, w0, w1, scales, T, K, N, E, rows_cap,
+                                        out);
+  return stream_launch<GATEUP, 8, W8>(dim3(gx, gy, chunks(128)), st, A, rv, w0, w1, scales, T, K, N, E, rows_cap,
+                                      out);
 }
 
-hipError_t launch_stream_down(int max_rows, int splits, const bf16_bits* H, RouteView rv, const void* wd,
-                              int64_t rows_cap, int d, int f, int E, float* Y, hipStream_t st) {
-  const dim3 grid((unsigned)E * (unsigned)(d / (kBW * 16)), (unsigned)splits);
-  if (max_rows <= 16) return stream_launch<false, 1>(grid, st, H, rv, wd, wd, 0, f, d, E, rows_cap, Y);
-  if (max_rows <= 32) return stream_launch<false, 2>(grid, st, H, rv, wd, wd, 0, f, d, E, rows_cap, Y);
-  return stream_launch<false, 4>(grid, st, H, rv, wd, wd, 0, f, d, E, rows_cap, Y);
+hipError_t launch_stream_gateup(int w8, int max_rows, const bf16_bits* x, RouteView rv, const void* wg,
+                                const void* wu, const float* scales, int64_t T, int d, int f, int E, bf16_bits* H,
+                                hipStream_t st) {
+  const unsigned gx = (unsigned)E * (unsigned)(f / (kBW * 8));
+  return w8 ? stream_dispatch<true, true>(max_rows, gx, 1u, st, x, rv, wg, wu, scales, T, d, f, E, 0, H)
+            : stream_dispatch<true, false>(max_rows, gx, 1u, st, x, rv, wg, wu, scales, T, d, f, E, 0, H);
+}
+
+hipError_t launch_stream_down(int w8, int max_rows, int splits, const bf16_bits* H, RouteView rv, const void* wd,
+                              const float* scales, int64_t rows_cap, int d, int f, int E, float* Y,
+                              hipStream_t st) {
+  const unsigned gx = (unsigned)E * (unsigned)(d / (kBW * 16));
+  return w8 ? stream_dispatch<false, true>(max_rows, gx, (unsigned)splits, st, H, rv, wd, wd, scales, 0, f, d, E,
+                                           rows_cap, Y)
+            : stream_dispatch<false, false>(max_rows, gx, (unsigned)splits, st, H, rv, wd, wd, scales, 0, f, d, E,
+                                            rows_cap, Y);
 }
 
 }  // namespace gmoe

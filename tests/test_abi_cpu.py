@@ -134,3 +134,15 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(gm, "LIB_PATH", "/nonexistent/libgrok_moe.so")
     with pytest.raises(RuntimeError, match="missing"):
         gm.lib()
+
+
+def test_build_rejects_scratch_kernels():
+    # the build fails when the compiler's resource-usage remark reports scratch memory for a kernel
+    from mixture_experts_transformer_gemm_amd.build import scratch_kernels
+    remarks = "\n".join([
+        "x.hip:1:1: remark: Function Name: _Z1av [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:2:1: remark: Function Name: _Z1bv [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:2:1: remark:     ScratchSize [bytes/lane]: 336 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert scratch_kernels(remarks) == [("_Z1bv", 336)]
