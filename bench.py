@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--tokens", type=int, default=0,
                     help="override the token count T (decode-shape sweep over T <= 64)")
+    ap.add_argument("--shard", choices=("tp8",), default=None,
+                    help="tp8: one GPU's share of the layer split 8 ways over the expert width (f = 32768/8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens the oracle times (0 = default per workload)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -94,12 +96,17 @@ def main():
 
     name = args.workload
     t0 = time.perf_counter()
-    w = synthetic.make(name, T=args.tokens or None)
+    f_override = None
+    if args.shard == "tp8":
+        f_override = synthetic.WORKLOADS[name][2] // 8
+    w = synthetic.make(name, T=args.tokens or None, f=f_override)
     log(f"generated {name} (T={w.T} d={w.d} f={w.f} E={w.E} k={w.k} weights {w.w_dtype}) in "
         f"{time.perf_counter() - t0:.1f}s")
     workload = WORKLOAD_NAMES[name]
     if args.tokens:
         workload = f"{workload.rsplit('_T', 1)[0]}_T{w.T}"
+    if args.shard:
+        workload += f"_{args.shard}_f{w.f}"
 
     def dev(a):
         if a is None:

@@ -31,9 +31,9 @@ def _sample_tokens(dbg, E, n_random, seed):
     return sorted(set(pick))
 
 
-def _run_and_check(name, n_random=8):
-    print(f"[fullsize] generating workload {name}", flush=True)
-    w = synthetic.make(name)
+def _run_and_check(name, n_random=8, T=None):
+    print(f"[fullsize] generating workload {name} (T={T or 'default'})", flush=True)
+    w = synthetic.make(name, T=T)
     print(f"[fullsize] {name}: T={w.T} d={w.d} f={w.f} E={w.E} k={w.k} weights={w.w_dtype}", flush=True)
     got, dbg = run_layer(w, torch)
     probs, oidx, _ = oracle.route(w.x, w.router_w, w.k)
@@ -59,6 +59,18 @@ def _run_and_check(name, n_random=8):
 
 def test_decode_full():
     dbg, counts = _run_and_check("decode")
+    assert counts.sum() == 16
+
+
+def test_decode_T64_full():
+    # 64-token decode: segments up to 64 rows in the weight-streaming kernel
+    dbg, counts = _run_and_check("decode", n_random=8, T=64)
+    assert counts.sum() == 128
+
+
+def test_int8_decode_full():
+    # 8-bit weights at decode size (weight streaming with int8 rows), every token checked
+    dbg, counts = _run_and_check("int8", T=8)
     assert counts.sum() == 16
 
 
