@@ -1,5 +1,6 @@
-// Weight-streaming grouped GEMMs for decode-sized batches (every expert
-// segment has at most 64 rows), gfx950.
+// Weight-streaming grouped GEMMs for small batches, gfx950: bf16 weights
+// with every expert segment of at most 64 rows, and 8-bit weights with
+// segments processed in chunks of up to 128 rows.
 //
 // In decode the layer is bound by reading the hit experts' weights from HBM
 // once (Grok-1 book ch. 1, section 1.2.1: generation moves the active weights
@@ -8,13 +9,17 @@
 // nontemporal hint, sustain about 7 TB/s, while 64-byte pieces of 16 rows per
 // instruction stay near 6 TB/s. So weight rows are streamed with
 // global_load_lds_dwordx4 in the 8-rows-x-128-bytes shape (lane i fetches 16
-// bytes of row i / 8) into an LDS ring of 6-8 stages and re-read from LDS in
-// the MFMA fragment layout.
+// bytes of row i / 8) into an LDS ring of 3-8 stages and re-read from LDS in
+// the MFMA fragment layout. A stage holds 128 bytes of each weight row: 64
+// reduction values of bf16 weights, 128 of 8-bit weights (Grok-1 book ch. 1,
+// section 1.2, the INT8 box: int8 values with a scale per group, dequantised
+// at compute time; here one fp32 scale per output channel, applied in the
+// epilogue).
 //
 // Workgroup = 8 wavefronts, each streaming its own 16 weight rows. The
 // segment's activation rows (token rows of x through the permutation, or H
-// rows) of each stage are loaded once per workgroup, one 8-row instruction
-// per wavefront for as many wavefronts as the segment needs, and shared by
+// rows) of each stage are loaded once per workgroup, spread over the
+// wavefronts for as many load instructions as the rows need, and shared by
 // all 8 wavefronts. Each wavefront waits for its own loads of a stage
 // (vmcnt), then one workgroup barrier makes the stage complete and frees the
 // slot read in the previous stage. MFMAs run only for the 16-row tiles that
@@ -30,7 +35,11 @@
 //
 // Fragment layout of v_mfma_f32_16x16x32_bf16: lane l supplies row (l mod 16)
 // and 8 reduction values of group l / 16; result register v of lane l is
-// C[4 (l / 16) + v][l mod 16] (weight row, activation row).
+// C[4 (l / 16) + v][l mod 16] (weight row, activation row). With 8-bit
+// weights a lane's 16-byte weight read holds 16 reduction values of two MFMA
+// steps (widened to bf16, exact); the activation fragment of each step is
+// read from the same reduction indices, so every product pairs equal
+// indices.
 #include "moe_device.h"
 
 #include <type_traits>
