@@ -60,12 +60,9 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ac
     p.path = PATH_TILED;
     // about k*T/E rows per expert: the tile height that wastes little of it
     p.bm = T <= 384 ? 64 : (T <= 1536 ? 128 : 256);
-#ifndef GMOE_W8_BM
-#define GMOE_W8_BM 128
-#endif
     // 8-bit weights: one row tile per expert up to 128 rows, so each weight
     // tile is streamed from HBM once
-    if (wdt == GROK_MOE_I8 && T <= 1536) p.bm = GMOE_W8_BM;
+    if (wdt == GROK_MOE_I8 && T <= 1536) p.bm = 128;
     // split the down projection's reduction while its tiles alone would
     // leave CUs idle: (row tiles upper bound) x (d / 256) tiles per split
     const int64_t tiles = (p.rows_cap / p.bm + E) * (d / 256);

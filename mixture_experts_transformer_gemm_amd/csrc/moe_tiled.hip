@@ -305,10 +305,14 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
       case 1: GMOE_WAIT_VM_LGKM0((NS - 2) * (D::QW + 1)); break;
       case 2: GMOE_WAIT_VM_LGKM0((NS - 2) * (D::QW + 2)); break;
       case 3: GMOE_WAIT_VM_LGKM0((NS - 2) * (D::QW + 3)); break;
-      default: GMOE_WAIT_VM_LGKM0((NS - 2) * (D::QW + 4)); break;
+      case 4: GMOE_WAIT_VM_LGKM0((NS - 2) * (D::QW + 4)); break;
+      case 5: GMOE_WAIT_VM_LGKM0((NS - 2) * (D::QW + 5)); break;
+      case 6: GMOE_WAIT_VM_LGKM0((NS - 2) * (D::QW + 6)); break;
+      case 7: GMOE_WAIT_VM_LGKM0((NS - 2) * (D::QW + 7)); break;
+      default: GMOE_WAIT_VM_LGKM0((NS - 2) * (D::QW + 8)); break;
     }
   };
-  static_assert(D::QA <= 4, "wait_stage covers up to 4 activation loads per stage");
+  static_assert(D::QA <= 8 && (NS - 2) * (D::QW + D::QA) <= 63, "wait_stage covers up to 8 activation loads");
 
   f32x16 acc[C::TI][C::TJ];
   zero_acc<BM, NW>(acc);
