@@ -13,7 +13,10 @@ of the pages it cites.
 Parity pins: routing, permutation, GELU, the expert FFN, the whole layer and
 the 8-bit scale indexing are each pinned by CPU tests (closed forms,
 invariants, brute force, textbook special cases and independent library
-routines). No function here is left unpinned.
+routines), and so are the variants (``layer``: SiLU experts, renormalised
+gates, capacity-factor drops, the sandwich sub-layer's RMSNorms and its bf16
+rounding of the pre-norm) in ``tests/test_oracle_variants.py``. No function
+here is left unpinned.
 """
 from __future__ import annotations
 
@@ -30,6 +33,17 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _handle = None
 
 F64, F32, BF16, I8 = 0, 1, 2, 3
+GELU, SILU = 0, 1
+
+
+class _Layer(ctypes.Structure):
+    # mirrors orc_layer in moe_oracle.c
+    _fields_ = [("x", ctypes.c_void_p), ("xdt", ctypes.c_int), ("router_w", ctypes.c_void_p), ("rdt", ctypes.c_int),
+                ("wg", ctypes.c_void_p), ("wu", ctypes.c_void_p), ("wd", ctypes.c_void_p), ("wdt", ctypes.c_int),
+                ("scales", ctypes.c_void_p), ("T", ctypes.c_int64), ("d", ctypes.c_int64), ("f", ctypes.c_int64),
+                ("E", ctypes.c_int), ("k", ctypes.c_int), ("act", ctypes.c_int), ("renormalize", ctypes.c_int),
+                ("capacity_factor", ctypes.c_double), ("norm_pre", ctypes.c_void_p),
+                ("norm_post", ctypes.c_void_p), ("norm_dt", ctypes.c_int), ("norm_eps", ctypes.c_double)]
 
 
 def build(force: bool = True) -> str:
@@ -58,8 +72,19 @@ def _lib():
                                                      vp, i64, vp, ci]
         lib.oracle_forward.argtypes = [vp, ci, vp, ci, vp, vp, vp, ci, vp, i64, i64, i64, ci, ci, vp, vp, vp, ci]
         lib.oracle_dense_onehot.argtypes = [vp, ci, vp, ci, vp, vp, vp, ci, vp, i64, i64, i64, ci, ci, vp, ci]
+        lib.oracle_silu.argtypes = [ctypes.c_double]
+        lib.oracle_silu.restype = ctypes.c_double
+        lib.oracle_bf16_rne.argtypes = [ctypes.c_double]
+        lib.oracle_bf16_rne.restype = ctypes.c_uint16
+        lib.oracle_capacity.argtypes = [ctypes.c_double, i64, ci, ci]
+        lib.oracle_capacity.restype = i64
+        lib.oracle_route_v.argtypes = [vp, ci, vp, ci, i64, i64, ci, ci, ci, vp, vp, vp, ci]
+        lib.oracle_permute_cap.argtypes = [vp, i64, ci, ci, i64, vp, vp, vp, vp]
+        lib.oracle_rmsnorm.argtypes = [vp, ci, i64, i64, vp, ci, ctypes.c_double, vp]
+        lib.oracle_layer.argtypes = [ctypes.POINTER(_Layer), vp, i64, vp, vp, vp, vp, vp, ci]
         for name in ("oracle_route", "oracle_permute", "oracle_expert", "oracle_forward_given_routing",
-                     "oracle_forward", "oracle_dense_onehot"):
+                     "oracle_forward", "oracle_dense_onehot", "oracle_route_v", "oracle_permute_cap",
+                     "oracle_rmsnorm", "oracle_layer"):
             getattr(lib, name).restype = ci
         _handle = lib
     return _handle
@@ -206,3 +231,97 @@ def dense_onehot(x, router_w, w_gate, w_up, w_down, k: int, scales=None, nthread
                                     T, d, f, E, k, out.ctypes.data, nthreads or threads())
     _check(rc, "dense_onehot")
     return out
+
+
+# ---------------------------------------------------------------- variants
+def silu(z: float) -> float:
+    return _lib().oracle_silu(float(z))
+
+
+def bf16_rne(v: float) -> int:
+    """Bit pattern of the bf16 value nearest to v (ties to even)."""
+    return int(_lib().oracle_bf16_rne(float(v)))
+
+
+def capacity(c: float, T: int, E: int, k: int) -> int:
+    """Rows each expert keeps under capacity factor c (-1: no cap, c <= 0)."""
+    return int(_lib().oracle_capacity(float(c), T, E, k))
+
+
+def route_v(x: np.ndarray, router_w: np.ndarray, k: int, renormalize: bool = False, nthreads: int = 0):
+    """route() with the optional renormalisation of the k gates."""
+    x = np.ascontiguousarray(x)
+    router_w = np.ascontiguousarray(router_w)
+    T, d = x.shape
+    E = router_w.shape[0]
+    probs = np.zeros((T, E), np.float64)
+    idx = np.zeros((T, k), np.int32)
+    gate = np.zeros((T, k), np.float64)
+    rc = _lib().oracle_route_v(x.ctypes.data, _dt(x, True), router_w.ctypes.data, _dt(router_w, True), T, d, E, k,
+                               int(bool(renormalize)), probs.ctypes.data, idx.ctypes.data, gate.ctypes.data,
+                               nthreads or threads())
+    _check(rc, "route_v")
+    return probs, idx, gate
+
+
+def permute_cap(idx: np.ndarray, E: int, cap: int):
+    """permute() with at most `cap` rows per expert (cap < 0: none). Dropped assignments get pos = -1;
+    perm holds offsets[E] valid rows (the rest of the array is zero)."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, k = idx.shape
+    counts = np.zeros(E, np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    perm = np.zeros(T * k, np.int32)
+    pos = np.zeros((T, k), np.int32)
+    rc = _lib().oracle_permute_cap(idx.ctypes.data, T, E, k, int(cap), counts.ctypes.data, offsets.ctypes.data,
+                                   perm.ctypes.data, pos.ctypes.data)
+    _check(rc, "permute_cap")
+    return counts, offsets, perm, pos
+
+
+def rmsnorm(v: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """Row-wise RMSNorm in double. uint16 arrays are bf16 bits."""
+    v = np.ascontiguousarray(v)
+    g = np.ascontiguousarray(g)
+    T, d = v.shape
+    out = np.zeros((T, d), np.float64)
+    rc = _lib().oracle_rmsnorm(v.ctypes.data, _dt(v, True), T, d, g.ctypes.data, _dt(g, True), float(eps),
+                               out.ctypes.data)
+    _check(rc, "rmsnorm")
+    return out
+
+
+def layer(x, router_w, w_gate, w_up, w_down, k: int, scales=None, activation: int = GELU,
+          renormalize: bool = False, capacity_factor: float = 0.0, norm_pre=None, norm_post=None,
+          norm_eps: float = 1e-5, tokens: Optional[Sequence[int]] = None, nthreads: int = 0):
+    """The layer with its variants. Returns dict(out [ntok, d] f64, idx, gate, pos [T, k], u [T, d] or None)."""
+    x = np.ascontiguousarray(x)
+    router_w = np.ascontiguousarray(router_w)
+    w_gate, w_up, w_down, wdt, scales = _wargs(w_gate, w_up, w_down, scales)
+    E, f, d = w_gate.shape
+    T = x.shape[0]
+    L = _Layer()
+    L.x, L.xdt = x.ctypes.data, _dt(x, True)
+    L.router_w, L.rdt = router_w.ctypes.data, _dt(router_w, True)
+    L.wg, L.wu, L.wd, L.wdt, L.scales = w_gate.ctypes.data, w_up.ctypes.data, w_down.ctypes.data, wdt, _c(scales)
+    L.T, L.d, L.f, L.E, L.k = T, d, f, E, k
+    L.act, L.renormalize, L.capacity_factor = int(activation), int(bool(renormalize)), float(capacity_factor)
+    u = None
+    if norm_pre is not None or norm_post is not None:
+        norm_pre = np.ascontiguousarray(norm_pre)
+        norm_post = np.ascontiguousarray(norm_post)
+        if norm_pre.dtype != norm_post.dtype:
+            raise TypeError("norm_pre and norm_post must share one dtype")
+        L.norm_pre, L.norm_post, L.norm_dt = norm_pre.ctypes.data, norm_post.ctypes.data, _dt(norm_pre, True)
+        u = np.zeros_like(x)
+    L.norm_eps = float(norm_eps)
+    tok = None if tokens is None else np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+    ntok = T if tok is None else tok.shape[0]
+    out = np.zeros((ntok, d), np.float64)
+    idx = np.zeros((T, k), np.int32)
+    gate = np.zeros((T, k), np.float64)
+    pos = np.zeros((T, k), np.int32)
+    rc = _lib().oracle_layer(ctypes.byref(L), _c(tok), ntok, out.ctypes.data, idx.ctypes.data, gate.ctypes.data,
+                             pos.ctypes.data, _c(u), nthreads or threads())
+    _check(rc, "layer")
+    return dict(out=out, idx=idx, gate=gate, pos=pos, u=u)

@@ -84,6 +84,11 @@ static int set_threads(int nthreads) {
  * (book ch. 10, section 10.4, GeGLU vs SwiGLU box). */
 double oracle_gelu(double z) { return 0.5 * z * (1.0 + erf(z / sqrt(2.0))); }
 
+/* SiLU: z * sigmoid(z), the activation of the SwiGLU experts that Mixtral and
+ * the later MoEs use in place of GELU (book ch. 10, section 10.4 table and
+ * the GeGLU vs SwiGLU box). */
+double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
+
 /* Steps 1-3 for one token: logits, softmax over all experts, top-k without
  * renormalisation (book ch. 10, section 10.3.1, the Grok-1 code). */
 static void route_token(const void* x, int xdt, const void* wr, int rdt, int64_t t, int64_t d, int E,
@@ -168,6 +173,7 @@ typedef struct {
   const float* scales;
   int64_t d, f;
   int E;
+  int act; /* 0: GELU (Grok-1), 1: SiLU (the SwiGLU variant) */
 } weights_t;
 
 static double w_gate(const weights_t* w, int e, int64_t j, int64_t i) {
@@ -195,7 +201,7 @@ static void expert_ffn(const weights_t* w, const double* x, int e, double* h, do
       a += x[i] * w_gate(w, e, j, i);
       b += x[i] * w_up(w, e, j, i);
     }
-    h[j] = oracle_gelu(a) * b;
+    h[j] = (w->act ? oracle_silu(a) : oracle_gelu(a)) * b;
   }
   for (int64_t i = 0; i < d; ++i) {
     double s = 0.0;
@@ -214,7 +220,7 @@ static int check_weights(int wdt, const float* scales) {
 int oracle_expert(const void* x, int xdt, int64_t t, const void* wg, const void* wu, const void* wd, int wdt,
                   const float* scales, int64_t d, int64_t f, int E, int e, double* y) {
   if (!check_weights(wdt, scales) || !valid_dt(xdt) || e < 0 || e >= E || d < 1 || f < 1) return ORC_EINVAL;
-  weights_t w = {wg, wu, wd, wdt, scales, d, f, E};
+  weights_t w = {wg, wu, wd, wdt, scales, d, f, E, 0};
   double* xr = (double*)malloc(sizeof(double) * (size_t)d);
   double* h = (double*)malloc(sizeof(double) * (size_t)f);
   if (!xr || !h) { free(xr); free(h); return ORC_ENOMEM; }
@@ -242,7 +248,7 @@ int oracle_forward_given_routing(const void* x, int xdt, const void* wg, const v
     for (int s = 0; s < k; ++s)
       if (idx[t * k + s] < 0 || idx[t * k + s] >= E) return ORC_EINVAL;
   }
-  weights_t w = {wg, wu, wd, wdt, scales, d, f, E};
+  weights_t w = {wg, wu, wd, wdt, scales, d, f, E, 0};
   /* y[r][s][:] = output of the expert in slot s for token tokens[r] */
   double* y = (double*)malloc(sizeof(double) * (size_t)(ntok * k * d));
   if (!y) return ORC_ENOMEM;
@@ -315,7 +321,7 @@ int oracle_dense_onehot(const void* x, int xdt, const void* router_w, int rdt, c
   if (!check_weights(wdt, scales) || !valid_dt(xdt) || T < 0 || d < 1 || f < 1 || E < 1 || E > 64 || k < 1 ||
       k > E)
     return ORC_EINVAL;
-  weights_t w = {wg, wu, wd, wdt, scales, d, f, E};
+  weights_t w = {wg, wu, wd, wdt, scales, d, f, E, 0};
   int nt = set_threads(nthreads);
   (void)nt;
   int fail = 0;
@@ -361,4 +367,253 @@ int oracle_dense_onehot(const void* x, int xdt, const void* router_w, int rdt, c
     free(ye);
   }
   return fail ? ORC_ENOMEM : ORC_OK;
+}
+
+/* ==================================================================== variants
+ * Layer variants the pages describe beside the Grok-1 default. Every knob at
+ * zero gives the Grok-1 layer above.
+ *  - act = 1: SiLU experts (SwiGLU; book ch. 10, section 10.4).
+ *  - renormalize: the k selected gates are divided by their sum, as Mixtral
+ *    does after its top-k (book ch. 10, section 10.3.1, the Mixtral code).
+ *  - capacity_factor c > 0: each expert takes at most c * k * T / E of the
+ *    k * T assignments, the rest are dropped and contribute nothing (book
+ *    ch. 10, section 10.3.2, the capacity factor box). The pages do not say
+ *    which assignments overflow; here an expert keeps those of its lowest
+ *    token indices (first come, first served in token order), and "at most
+ *    c*k*T/E" is the integer floor of that bound.
+ *  - norm_pre and norm_post: the sandwich sub-layer (field guide, "数据怎样流
+ *    过 64 层": the sub-layer normalises, runs the MoE, and adds the gated sum
+ *    back to the trunk; book ch. 11, list of what Grok-1 left behind: two
+ *    norms per sub-layer; book ch. 10, section 10.3.1: the post-norm bounds
+ *    the output that un-normalised gates leave unscaled):
+ *        u   = RMSNorm(x; norm_pre), stored in the activation type
+ *        out = x + RMSNorm(MoE(u); norm_post)
+ *    with RMSNorm(v; g)[i] = g[i] * v[i] / sqrt(mean_j v[j]^2 + eps). u is
+ *    rounded to the activation type (bf16 or fp32, round to nearest even)
+ *    because the router and the experts consume it as a stored tensor of a
+ *    bf16 forward pass; MoE(u) and the post-norm stay in double. */
+
+/* Round to the nearest bf16 value (8 significant bits), ties to even; returns
+ * the bit pattern. Normal range only (|v| in [2^-126, 2^128)) and zero. */
+uint16_t oracle_bf16_rne(double v) {
+  if (v == 0.0) return signbit(v) ? 0x8000u : 0u;
+  int e;
+  double m = frexp(fabs(v), &e);          /* |v| = m * 2^e, m in [0.5, 1) */
+  double r = nearbyint(ldexp(m, 8));      /* 8 significant bits, ties to even */
+  float q = (float)ldexp(r, e - 8);       /* exact: 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &q, 4);
+  return (uint16_t)((u >> 16) | (v < 0.0 ? 0x8000u : 0u));
+}
+
+/* Rows per expert under capacity factor c, or -1 (no cap) when c <= 0. */
+int64_t oracle_capacity(double c, int64_t T, int E, int k) {
+  if (!(c > 0.0)) return -1;
+  return (int64_t)floor(c * (double)(k * T) / (double)E);
+}
+
+/* Routing with the optional renormalisation: gates divided by their sum over
+ * the k slots (summed in slot order). */
+int oracle_route_v(const void* x, int xdt, const void* router_w, int rdt, int64_t T, int64_t d, int E, int k,
+                   int renormalize, double* probs, int32_t* idx, double* gate, int nthreads) {
+  int rc = oracle_route(x, xdt, router_w, rdt, T, d, E, k, probs, idx, gate, nthreads);
+  if (rc != ORC_OK || !renormalize) return rc;
+  for (int64_t t = 0; t < T; ++t) {
+    double sum = 0.0;
+    for (int s = 0; s < k; ++s) sum += gate[t * k + s];
+    for (int s = 0; s < k; ++s) gate[t * k + s] /= sum;
+  }
+  return ORC_OK;
+}
+
+/* Permutation with a per-expert cap (cap < 0: none). For every expert, its
+ * assignments are ranked by token index; those of rank >= cap are dropped
+ * (pos = -1, no row). counts are the kept assignments, offsets their
+ * exclusive scan, and segment e lists its kept tokens in ascending order. */
+int oracle_permute_cap(const int32_t* idx, int64_t T, int E, int k, int64_t cap, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* pos) {
+  if (T < 0 || E < 1 || k < 1 || k > E || !counts || !offsets) return ORC_EINVAL;
+  int64_t* seen = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+  if (!seen) return ORC_ENOMEM;
+  /* pass 1: how many assignments each expert has, and how many it keeps */
+  for (int64_t a = 0; a < T * k; ++a) {
+    int e = idx[a];
+    if (e < 0 || e >= E) { free(seen); return ORC_EINVAL; }
+    seen[e] += 1;
+  }
+  for (int e = 0; e < E; ++e) counts[e] = (int32_t)((cap >= 0 && seen[e] > cap) ? cap : seen[e]);
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  /* pass 2: walk the tokens in order; an expert's rank-th assignment gets row
+   * offsets[e] + rank while rank < counts[e] */
+  for (int e = 0; e < E; ++e) seen[e] = 0;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int s = 0; s < k; ++s) {
+      int e = idx[t * k + s];
+      int64_t rank = seen[e]++;
+      if (rank < counts[e]) {
+        int32_t row = (int32_t)(offsets[e] + rank);
+        perm[row] = (int32_t)t;
+        pos[t * k + s] = row;
+      } else {
+        pos[t * k + s] = -1;
+      }
+    }
+  }
+  free(seen);
+  return ORC_OK;
+}
+
+/* RMSNorm of each of the T rows of v (d values): out[t][i] = g[i] * v[t][i] *
+ * r_t, r_t = 1 / sqrt(mean_i v[t][i]^2 + eps), all in double. */
+int oracle_rmsnorm(const void* v, int vdt, int64_t T, int64_t d, const void* g, int gdt, double eps, double* out) {
+  if (T < 0 || d < 1 || !valid_dt(vdt) || !valid_dt(gdt) || !(eps >= 0.0)) return ORC_EINVAL;
+  for (int64_t t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int64_t i = 0; i < d; ++i) {
+      double a = elem(v, vdt, t * d + i);
+      ss += a * a;
+    }
+    double r = 1.0 / sqrt(ss / (double)d + eps);
+    for (int64_t i = 0; i < d; ++i) out[t * d + i] = (elem(v, vdt, t * d + i) * r) * elem(g, gdt, i);
+  }
+  return ORC_OK;
+}
+
+/* Every input of one layer call, with the variant knobs. */
+typedef struct {
+  const void* x;
+  int xdt; /* ORC_BF16 or ORC_F32: also the type u is stored in */
+  const void* router_w;
+  int rdt;
+  const void *wg, *wu, *wd;
+  int wdt;
+  const float* scales;
+  int64_t T, d, f;
+  int E, k;
+  int act;
+  int renormalize;
+  double capacity_factor;
+  const void* norm_pre; /* both NULL, or both [d] of type norm_dt */
+  const void* norm_post;
+  int norm_dt;
+  double norm_eps;
+} orc_layer;
+
+/* The layer with its variants: routing and permutation for all T tokens, then
+ * the outputs of the listed tokens (all T when tokens is NULL; ntok rows of d
+ * values in out). Optional outputs: idx/gate [T][k], pos [T][k] (-1 =
+ * dropped), u (T*d values of type xdt, the stored pre-norm output). */
+int oracle_layer(const orc_layer* L, const int64_t* tokens, int64_t ntok, double* out, int32_t* idx_out,
+                 double* gate_out, int32_t* pos_out, void* u_out, int nthreads) {
+  if (!L || L->T < 0 || L->d < 1 || L->f < 1 || L->E < 1 || L->E > 64 || L->k < 1 || L->k > L->E) return ORC_EINVAL;
+  if (L->xdt != ORC_BF16 && L->xdt != ORC_F32) return ORC_EINVAL;
+  if (!check_weights(L->wdt, L->scales) || (L->act != 0 && L->act != 1)) return ORC_EINVAL;
+  if ((L->norm_pre == NULL) != (L->norm_post == NULL)) return ORC_EINVAL;
+  const int sandwich = L->norm_pre != NULL;
+  if (sandwich && (!valid_dt(L->norm_dt) || !(L->norm_eps >= 0.0))) return ORC_EINVAL;
+  if (!tokens && ntok != L->T) return ORC_EINVAL;
+  const int64_t T = L->T, d = L->d, f = L->f;
+  const int E = L->E, k = L->k;
+  if (T == 0) return ORC_OK;
+  for (int64_t r = 0; r < ntok; ++r)
+    if (tokens && (tokens[r] < 0 || tokens[r] >= T)) return ORC_EINVAL;
+
+  const size_t esz = L->xdt == ORC_BF16 ? 2 : 4;
+  void* u = NULL;
+  double* tmp = NULL;
+  int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * k));
+  double* gate = (double*)malloc(sizeof(double) * (size_t)(T * k));
+  int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * k));
+  int32_t* perm = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * k));
+  int32_t counts[64], offsets[65];
+  double* y = (double*)malloc(sizeof(double) * (size_t)(ntok * k * d + 1));
+  int rc = ORC_ENOMEM;
+  if (!idx || !gate || !pos || !perm || !y) goto done;
+
+  /* 1. the MoE input: x, or the pre-norm of x stored in the activation type */
+  const void* a = L->x;
+  if (sandwich) {
+    u = malloc(esz * (size_t)(T * d));
+    tmp = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!u || !tmp) goto done;
+    for (int64_t t = 0; t < T; ++t) {
+      rc = oracle_rmsnorm((const char*)L->x + esz * (size_t)(t * d), L->xdt, 1, d, L->norm_pre, L->norm_dt,
+                          L->norm_eps, tmp);
+      if (rc != ORC_OK) goto done;
+      for (int64_t i = 0; i < d; ++i) {
+        if (L->xdt == ORC_BF16) ((uint16_t*)u)[t * d + i] = oracle_bf16_rne(tmp[i]);
+        else ((float*)u)[t * d + i] = (float)tmp[i];
+      }
+    }
+    a = u;
+  }
+  /* 2. routing (softmax, top-k, optional renormalisation) */
+  rc = oracle_route_v(a, L->xdt, L->router_w, L->rdt, T, d, E, k, L->renormalize, NULL, idx, gate, nthreads);
+  if (rc != ORC_OK) goto done;
+  /* 3. permutation with the capacity cap: decides which assignments run */
+  rc = oracle_permute_cap(idx, T, E, k, oracle_capacity(L->capacity_factor, T, E, k), counts, offsets, perm, pos);
+  if (rc != ORC_OK) goto done;
+  /* 4. expert outputs of the kept assignments of the listed tokens */
+  {
+    weights_t w = {L->wg, L->wu, L->wd, L->wdt, L->scales, d, f, E, L->act};
+    int nt = set_threads(nthreads);
+    (void)nt;
+    int fail = 0;
+#pragma omp parallel num_threads(nt)
+    {
+      double* xr = (double*)malloc(sizeof(double) * (size_t)d);
+      double* h = (double*)malloc(sizeof(double) * (size_t)f);
+      if (!xr || !h) {
+#pragma omp atomic write
+        fail = 1;
+      } else {
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t q = 0; q < ntok * k; ++q) {
+          int64_t r = q / k;
+          int s = (int)(q % k);
+          int64_t t = tokens ? tokens[r] : r;
+          if (pos[t * k + s] < 0) {
+            for (int64_t i = 0; i < d; ++i) y[q * d + i] = 0.0;
+            continue;
+          }
+          for (int64_t i = 0; i < d; ++i) xr[i] = elem(a, L->xdt, t * d + i);
+          expert_ffn(&w, xr, idx[t * k + s], h, y + q * d);
+        }
+      }
+      free(xr);
+      free(h);
+    }
+    if (fail) { rc = ORC_ENOMEM; goto done; }
+  }
+  /* 5. gated sum over the kept slots, then the post-norm and the residual */
+  for (int64_t r = 0; r < ntok; ++r) {
+    int64_t t = tokens ? tokens[r] : r;
+    double* o = out + r * d;
+    for (int64_t i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (int s = 0; s < k; ++s)
+        if (pos[t * k + s] >= 0) acc += gate[t * k + s] * y[(r * k + s) * d + i];
+      o[i] = acc;
+    }
+    if (sandwich) {
+      rc = oracle_rmsnorm(o, ORC_F64, 1, d, L->norm_post, L->norm_dt, L->norm_eps, tmp);
+      if (rc != ORC_OK) goto done;
+      for (int64_t i = 0; i < d; ++i) o[i] = elem(L->x, L->xdt, t * d + i) + tmp[i];
+    }
+  }
+  if (idx_out) memcpy(idx_out, idx, sizeof(int32_t) * (size_t)(T * k));
+  if (gate_out) memcpy(gate_out, gate, sizeof(double) * (size_t)(T * k));
+  if (pos_out) memcpy(pos_out, pos, sizeof(int32_t) * (size_t)(T * k));
+  if (u_out && u) memcpy(u_out, u, esz * (size_t)(T * d));
+  rc = ORC_OK;
+done:
+  free(idx);
+  free(gate);
+  free(pos);
+  free(perm);
+  free(y);
+  free(u);
+  free(tmp);
+  return rc;
 }

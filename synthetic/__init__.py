@@ -22,7 +22,13 @@ Storage layouts (all row-major, contiguous):
   channel (8-bit workload only); the real weight is q * scale.
 
 Tensor ids for the counter-based generator: x=0, router=1, gate=2, up=3,
-down=4.
+down=4, pre-norm weights=5, post-norm weights=6 (7: the test-only random
+scales).
+
+Variants beside the Grok-1 layer: the Mixtral 8x22B shape (d = 6144,
+f = 16384, 8 experts, top-2; book ch. 10, section 10.1 table) with SiLU
+experts and renormalised gates; the sandwich sub-layer (RMSNorm weights
+before and after the MoE); a capacity factor.
 """
 from __future__ import annotations
 
@@ -40,7 +46,7 @@ _SRC = os.path.join(_HERE, "philox_gen.c")
 _LIB = os.path.join(_HERE, "libsynthetic.so")
 _lib_handle = None
 
-TID_X, TID_ROUTER, TID_GATE, TID_UP, TID_DOWN = 0, 1, 2, 3, 4
+TID_X, TID_ROUTER, TID_GATE, TID_UP, TID_DOWN, TID_NORM_PRE, TID_NORM_POST = 0, 1, 2, 3, 4, 5, 6
 
 
 def build(force: bool = True) -> str:
@@ -139,6 +145,12 @@ class Workload:
     scales: Optional[np.ndarray] = None
     seed: int = 0
     notes: Dict[str, str] = field(default_factory=dict)
+    activation: str = "gelu"            # "gelu" | "silu"
+    renormalize: bool = False
+    capacity_factor: float = 0.0        # 0: no cap
+    norm_pre: Optional[np.ndarray] = None   # [d], activation dtype (sandwich sub-layer)
+    norm_post: Optional[np.ndarray] = None
+    norm_eps: float = 1e-5
 
     @property
     def weight_bytes(self) -> int:
@@ -157,7 +169,25 @@ WORKLOADS = {
     "int8": (256, 6144, 32768, 8, 2, "bf16", "i8", False),
     # Grok-1-shape layer with router logits biased toward experts 0 and 1.
     "skew": (2048, 6144, 32768, 8, 2, "bf16", "bf16", True),
+    # Mixtral 8x22B-shape decode step and full-context prefill (SiLU, renormalised gates).
+    "mixtral_decode": (8, 6144, 16384, 8, 2, "bf16", "bf16", False),
+    "mixtral_prefill": (8192, 6144, 16384, 8, 2, "bf16", "bf16", False),
 }
+
+# name -> variant knobs that differ from the Grok-1 layer
+VARIANTS = {
+    "mixtral_decode": dict(activation="silu", renormalize=True),
+    "mixtral_prefill": dict(activation="silu", renormalize=True),
+}
+
+
+def norm_weights(d: int, seed: int, dtype: str = "bf16"):
+    """RMSNorm weights of the sandwich sub-layer: 1 + 0.1 z per channel, z ~ N(0, 1), rounded to `dtype`."""
+    out = []
+    for tid in (TID_NORM_PRE, TID_NORM_POST):
+        g = 1.0 + normal((d,), seed, tid, 0.1, "f32")
+        out.append(g.astype(np.float32) if dtype == "f32" else f32_to_bf16_bits(g.astype(np.float32)))
+    return out[0], out[1]
 
 # Skew construction: feature d-1 of every token is 1.0 and the router row of
 # expert e carries SKEW_BIAS[e] at feature d-1, so logit e gains exactly that
@@ -168,10 +198,13 @@ SKEW_BIAS = (3.0, 1.5)
 def make(name: str = "decode", seed: int = 0, T: Optional[int] = None, d: Optional[int] = None,
          f: Optional[int] = None, E: Optional[int] = None, k: Optional[int] = None,
          act_dtype: Optional[str] = None, w_dtype: Optional[str] = None,
-         skew: Optional[bool] = None, with_weights: bool = True) -> Workload:
-    """Build a named workload; any size or dtype can be overridden (for small parity cases).
+         skew: Optional[bool] = None, with_weights: bool = True, activation: Optional[str] = None,
+         renormalize: Optional[bool] = None, capacity_factor: Optional[float] = None,
+         sandwich: bool = False, norm_eps: float = 1e-5) -> Workload:
+    """Build a named workload; any size, dtype or variant knob can be overridden (for small parity cases).
 
     with_weights=False leaves the expert weights as empty placeholders (routing-only checks).
+    sandwich=True adds the RMSNorm weights of the sandwich sub-layer.
     """
     T0, d0, f0, E0, k0, a0, w0, s0 = WORKLOADS[name]
     T = T0 if T is None else T
@@ -216,9 +249,22 @@ def make(name: str = "decode", seed: int = 0, T: Optional[int] = None, d: Option
         else:
             router_w[:, d - 1] = f32_to_bf16_bits(bias)
         notes["skew"] = "x[:, d-1] = 1.0; router_w[:, d-1] = (+3.0, +1.5, 0, ...)"
+    var = dict(activation="gelu", renormalize=False, capacity_factor=0.0)
+    var.update(VARIANTS.get(name, {}))
+    if activation is not None:
+        var["activation"] = activation
+    if renormalize is not None:
+        var["renormalize"] = renormalize
+    if capacity_factor is not None:
+        var["capacity_factor"] = capacity_factor
+    if var["activation"] not in ("gelu", "silu"):
+        raise ValueError(f"unknown activation {var['activation']}")
+    norm_pre = norm_post = None
+    if sandwich:
+        norm_pre, norm_post = norm_weights(d, seed, act)
     return Workload(name=name, T=T, d=d, f=f, E=E, k=k, act_dtype=act, w_dtype=wdt, x=x,
                     router_w=router_w, w_gate=w_gate, w_up=w_up, w_down=w_down, scales=scales,
-                    seed=seed, notes=notes)
+                    seed=seed, notes=notes, norm_pre=norm_pre, norm_post=norm_post, norm_eps=norm_eps, **var)
 
 
 def random_scales(E: int, d: int, f: int, seed: int, tensor_id: int = 7) -> np.ndarray:
