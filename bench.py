@@ -10,6 +10,10 @@ experts' weights from HBM.
 Prints one JSON line with the whole-job throughput (tokens/s), the roofline of
 the dominant kernel measured live with HIP events on the launch stream, and
 the CPU oracle timed on the host as a reported baseline.
+
+Variants (not the headline): --workload mixtral_decode / mixtral_prefill (Mixtral
+8x22B expert shapes, SiLU experts, renormalised gates), --sandwich (RMSNorm
+before and after the MoE plus the residual), --capacity c (capacity factor).
 """
 from __future__ import annotations
 
@@ -35,6 +39,8 @@ WORKLOAD_NAMES = {
     "int8": "grok1_moe_layer_int8w_T256",
     "skew": "grok1_moe_layer_skewed_T2048",
     "tiny_f32": "tiny_moe_layer_f32_T64",
+    "mixtral_decode": "mixtral8x22b_moe_layer_decode_T8",
+    "mixtral_prefill": "mixtral8x22b_moe_layer_prefill_T8192",
 }
 
 
@@ -50,8 +56,13 @@ def parse():
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--tokens", type=int, default=0,
                     help="override the token count T (decode-shape sweep over T <= 64)")
-    ap.add_argument("--shard", choices=("tp8",), default=None,
-                    help="tp8: one GPU's share of the layer split 8 ways over the expert width (f = 32768/8)")
+    ap.add_argument("--shard", choices=("tp8", "ep8"), default=None,
+                    help="tp8: one GPU's share of the layer split 8 ways over the expert width (f/8); "
+                         "ep8: one GPU's share under expert parallelism (the busiest expert with its routed rows)")
+    ap.add_argument("--sandwich", action="store_true",
+                    help="the sandwich sub-layer: out = x + RMSNorm(MoE(RMSNorm(x)))")
+    ap.add_argument("--capacity", type=float, default=0.0,
+                    help="capacity factor c > 0: each expert runs at most floor(c*k*T/E) assignments")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens the oracle times (0 = default per workload)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -99,14 +110,20 @@ def main():
     f_override = None
     if args.shard == "tp8":
         f_override = synthetic.WORKLOADS[name][2] // 8
-    w = synthetic.make(name, T=args.tokens or None, f=f_override)
-    log(f"generated {name} (T={w.T} d={w.d} f={w.f} E={w.E} k={w.k} weights {w.w_dtype}) in "
+    w = synthetic.make(name, T=args.tokens or None, f=f_override, sandwich=args.sandwich,
+                       capacity_factor=args.capacity or None)
+    log(f"generated {name} (T={w.T} d={w.d} f={w.f} E={w.E} k={w.k} weights {w.w_dtype} act {w.activation} "
+        f"renorm {w.renormalize} capacity {w.capacity_factor} sandwich {args.sandwich}) in "
         f"{time.perf_counter() - t0:.1f}s")
     workload = WORKLOAD_NAMES[name]
     if args.tokens:
         workload = f"{workload.rsplit('_T', 1)[0]}_T{w.T}"
-    if args.shard:
+    if args.shard == "tp8":
         workload += f"_{args.shard}_f{w.f}"
+    if args.sandwich:
+        workload += "_sandwich"
+    if w.capacity_factor:
+        workload += f"_cap{w.capacity_factor:g}"
 
     def dev(a):
         if a is None:
@@ -115,7 +132,10 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(a).cuda()
 
-    x, rw, wg, wu, wd, sc = (dev(getattr(w, n)) for n in ("x", "router_w", "w_gate", "w_up", "w_down", "scales"))
+    x, rw, wg, wu, wd, sc, npre, npost = (dev(getattr(w, n)) for n in ("x", "router_w", "w_gate", "w_up", "w_down",
+                                                                       "scales", "norm_pre", "norm_post"))
+    variant = dict(activation=gm.ACT_SILU if w.activation == "silu" else gm.ACT_GELU, renormalize=w.renormalize,
+                   capacity_factor=w.capacity_factor, norm_pre=npre, norm_post=npost, norm_eps=w.norm_eps)
     torch.cuda.synchronize()
     log("inputs resident in HBM")
     out = torch.empty_like(x)
@@ -124,15 +144,43 @@ def main():
     stream = torch.cuda.current_stream()
 
     # routing of this batch (for the algorithmic byte count: only hit experts are read)
-    _, dbg = gm.grok_moe_forward_ex(x, rw, wg, wu, wd, k=w.k, scales=sc, out=out, workspace=ws, debug=True)
+    _, dbg = gm.grok_moe_forward_ex(x, rw, wg, wu, wd, k=w.k, scales=sc, out=out, workspace=ws, debug=True, **variant)
     torch.cuda.synchronize()
     counts = dbg["counts"].cpu().numpy()
+    if args.shard == "ep8":
+        # one expert per GPU: the busiest expert's GPU runs that expert on its routed rows
+        # (gate 1 with E = 1, k = 1); the all-to-all that brings the rows is not modelled
+        import dataclasses
+        e = int(np.argmax(counts))
+        offs, perm = dbg["offsets"].cpu().numpy(), dbg["perm"].cpu().numpy()
+        tok = perm[offs[e]:offs[e + 1]].astype(np.int64)
+        E0, f0, d0 = w.E, w.f, w.d
+        sc_e = None
+        if w.scales is not None:   # per-channel scales of expert e: [gate f | up f | down d]
+            sc_e = np.concatenate([w.scales[e * f0:(e + 1) * f0], w.scales[E0 * f0 + e * f0:E0 * f0 + (e + 1) * f0],
+                                   w.scales[2 * E0 * f0 + e * d0:2 * E0 * f0 + (e + 1) * d0]])
+            sc = torch.from_numpy(sc_e).cuda()
+        w = dataclasses.replace(w, T=len(tok), E=1, k=1, x=w.x[tok], router_w=w.router_w[e:e + 1],
+                                w_gate=w.w_gate[e:e + 1], w_up=w.w_up[e:e + 1], w_down=w.w_down[e:e + 1],
+                                scales=sc_e, renormalize=False, capacity_factor=0.0)
+        ti = torch.from_numpy(tok).cuda()
+        x, rw, wg, wu, wd = x[ti].contiguous(), rw[e:e + 1], wg[e:e + 1], wu[e:e + 1], wd[e:e + 1]
+        variant.update(renormalize=False, capacity_factor=0.0)
+        workload += f"_ep8_expert{e}_M{w.T}"
+        log(f"expert-parallel share: expert {e}, {w.T} rows")
+        out = torch.empty_like(x)
+        need = gm.grok_moe_workspace_bytes(w.T, w.d, w.f, 1, 1, gm._dtype_code(x), gm._dtype_code(wg))
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        _, dbg = gm.grok_moe_forward_ex(x, rw, wg, wu, wd, k=1, scales=sc, out=out, workspace=ws, debug=True,
+                                        **variant)
+        torch.cuda.synchronize()
+        counts = dbg["counts"].cpu().numpy()
     n_hit = int(np.sum(counts > 0))
     rows = int(counts.sum())
 
     def step(events=None):
         gm.grok_moe_forward_ex(x, rw, wg, wu, wd, k=w.k, scales=sc, out=out, workspace=ws, events=events,
-                               stream=stream)
+                               stream=stream, **variant)
 
     for _ in range(args.warmup):
         step()
@@ -178,7 +226,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
     roof["traffic"], traffic_note = measured_traffic(workload)
-    roof.update({"kernel": "gate_up grouped GEMM (+GELU*up)",
+    roof.update({"kernel": "gate_up grouped GEMM (+" + ("SiLU" if w.activation == "silu" else "GELU") + "*up)",
                  "algorithmic_per_launch": gu_bytes if hbm_bound else gu_flops,
                  "avg_launch_ms": round(stage_ms["gate_up"], 5), "traffic_source": traffic_note})
 
@@ -200,7 +248,9 @@ def main():
         "dtype": {"bf16": "bf16", "i8": "int8w-bf16", "f32": "f32"}[w.w_dtype],
         "data": "synthetic",
         "config": {"workload": workload, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k,
-                   "weights": w.w_dtype, "experts_hit": n_hit},
+                   "weights": w.w_dtype, "experts_hit": n_hit, "activation": w.activation,
+                   "renormalize": w.renormalize, "capacity_factor": w.capacity_factor, "sandwich": args.sandwich,
+                   "rows_run": rows},
         "roofline": roof,
         "cpu_baseline": cpu,
         "layer": {"ms": round(ms_per_step, 5), "GBps": round(layer_bytes / (ms_per_step / 1e3) / 1e9, 1),
@@ -222,12 +272,15 @@ def cpu_baseline(w, name, args):
     passes, dt = 0, 0.0
     t0 = time.perf_counter()
     while passes == 0 or (dt < args.cpu_seconds and passes < 100000):
-        oracle.forward(w.x[:n], w.router_w, w.w_gate, w.w_up, w.w_down, w.k, scales=w.scales, nthreads=cores)
+        oracle.layer(w.x[:n], w.router_w, w.w_gate, w.w_up, w.w_down, w.k, scales=w.scales,
+                     activation=oracle.SILU if w.activation == "silu" else oracle.GELU, renormalize=w.renormalize,
+                     capacity_factor=w.capacity_factor, norm_pre=w.norm_pre, norm_post=w.norm_post,
+                     norm_eps=w.norm_eps, nthreads=cores)
         passes += 1
         dt = time.perf_counter() - t0
     return {"value": round(n * passes / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {n} of the {w.T} tokens, {passes} pass(es), whole layer (routing, {w.k} experts "
-                      f"per token, combine) in fp64: {dt:.2f} s"}
+            "sample": f"first {n} of the {w.T} tokens as their own batch, {passes} pass(es), whole layer "
+                      f"(routing, {w.k} experts per token, combine) in fp64: {dt:.2f} s"}
 
 
 def _source_digest(files):

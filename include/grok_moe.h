@@ -68,6 +68,12 @@ typedef enum {
 /* element types */
 enum { GROK_MOE_BF16 = 0, GROK_MOE_F32 = 1, GROK_MOE_I8 = 2 };
 
+/* activation of the gate branch: GELU with the exact Gaussian CDF (Grok-1's
+ * GeGLU experts) or SiLU, z * sigmoid(z) (the SwiGLU experts of Mixtral and
+ * others; book ch. 10, section 10.4, the expert-structure table and the
+ * GeGLU vs SwiGLU box) */
+enum { GROK_MOE_ACT_GELU = 0, GROK_MOE_ACT_SILU = 1 };
+
 /* Full argument set of one layer call. act_dtype is the type of x, router_w
  * and out (GROK_MOE_BF16 or GROK_MOE_F32); w_dtype the type of the expert
  * weights (GROK_MOE_BF16 with bf16 activations, GROK_MOE_I8 with bf16
@@ -76,7 +82,28 @@ enum { GROK_MOE_BF16 = 0, GROK_MOE_F32 = 1, GROK_MOE_I8 = 2 };
  * indices, fp32 gates). When route_idx is non-NULL the router is skipped and
  * this routing is used instead (router_w may then be NULL); each row must
  * hold k distinct indices in [0, E) (an index outside that range is dropped
- * and contributes nothing). */
+ * and contributes nothing).
+ *
+ * Variants (a zero-filled tail after route_gate is the Grok-1 layer):
+ *  activation       GROK_MOE_ACT_GELU or GROK_MOE_ACT_SILU.
+ *  renormalize      non-zero: the router's k gates are divided by their sum
+ *                   (Mixtral; book ch. 10, section 10.3.1, the Mixtral code).
+ *                   Gates given in route_gate are used as they are.
+ *  capacity_factor  > 0: each expert runs at most floor(c * k * T / E) of the
+ *                   k*T assignments, those of its lowest token indices; the
+ *                   rest are dropped and contribute nothing (book ch. 10,
+ *                   section 10.3.2, the capacity factor box). 0: no cap.
+ *                   Negative or NaN: GROK_MOE_EINVAL.
+ *  norm_pre,        both NULL, or both [d] arrays of the activation type:
+ *  norm_post        the sandwich sub-layer (field guide, the data-flow
+ *                   section; book ch. 10, section 10.3.1 on the post-norm):
+ *                     u   = RMSNorm(x; norm_pre), stored in the activation type
+ *                     out = x + RMSNorm(MoE(u); norm_post)
+ *                   with RMSNorm(v; g)[i] = g[i] v[i] / sqrt(mean(v^2) + eps);
+ *                   the router and the experts see u. Dropped assignments
+ *                   leave a token's MoE sum at zero, so out = x for a token
+ *                   whose every assignment overflowed.
+ *  norm_eps         eps of both norms (>= 0, finite). */
 typedef struct grok_moe_args {
   const void* x;
   const void* router_w;
@@ -90,6 +117,12 @@ typedef struct grok_moe_args {
   int32_t act_dtype, w_dtype;
   const int32_t* route_idx;
   const float* route_gate;
+  int32_t activation;
+  int32_t renormalize;
+  double capacity_factor;
+  const void* norm_pre;
+  const void* norm_post;
+  double norm_eps;
 } grok_moe_args;
 
 /* Optional outputs for tests and profiling (every field may be NULL).
@@ -97,10 +130,12 @@ typedef struct grok_moe_args {
  *   idx [T][k] int32, gate [T][k] fp32  - the routing
  *   counts [E], offsets [E+1] int32     - rows per expert and their exclusive scan
  *   perm [k*T] int32                    - row -> token (segment e in ascending token order)
- *   pos [T][k] int32                    - (token, slot) -> row
+ *   pos [T][k] int32                    - (token, slot) -> row, -1 if dropped
+ *   u [T][d] activation type            - the pre-norm output (sandwich only)
  * events: hipEvent_t handles; when events[i] is non-NULL it is recorded on the
- * stream before stage i (0 router, 1 permutation, 2 gate/up GEMM, 3 down
- * GEMM, 4 combine) and events[5] after the last stage. */
+ * stream before stage i (0 router, with the pre-norm when there is one, 1
+ * permutation, 2 gate/up GEMM, 3 down GEMM, 4 combine) and events[5] after the
+ * last stage. */
 typedef struct grok_moe_debug {
   int32_t* idx;
   float* gate;
@@ -109,6 +144,7 @@ typedef struct grok_moe_debug {
   int32_t* perm;
   int32_t* pos;
   void* events[6];
+  void* u;
 } grok_moe_debug;
 
 /* Bytes of device workspace grok_moe_forward_ex needs for this shape, or 0 for

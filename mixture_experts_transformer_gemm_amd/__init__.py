@@ -25,6 +25,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgrok_moe.so")
 
 BF16, F32, I8 = 0, 1, 2
+ACT_GELU, ACT_SILU = 0, 1
 OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
 STAGES = ("router", "permute", "gate_up", "down", "combine")
 
@@ -43,13 +44,15 @@ class Args(ctypes.Structure):
                 ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("out", ctypes.c_void_p), ("T", ctypes.c_int64), ("d", ctypes.c_int64), ("f", ctypes.c_int64),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("w_dtype", ctypes.c_int32), ("route_idx", ctypes.c_void_p), ("route_gate", ctypes.c_void_p)]
+                ("w_dtype", ctypes.c_int32), ("route_idx", ctypes.c_void_p), ("route_gate", ctypes.c_void_p),
+                ("activation", ctypes.c_int32), ("renormalize", ctypes.c_int32), ("capacity_factor", ctypes.c_double),
+                ("norm_pre", ctypes.c_void_p), ("norm_post", ctypes.c_void_p), ("norm_eps", ctypes.c_double)]
 
 
 class Debug(ctypes.Structure):
     _fields_ = [("idx", ctypes.c_void_p), ("gate", ctypes.c_void_p), ("counts", ctypes.c_void_p),
                 ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("pos", ctypes.c_void_p),
-                ("events", ctypes.c_void_p * 6)]
+                ("events", ctypes.c_void_p * 6), ("u", ctypes.c_void_p)]
 
 
 _lib_handle = None
@@ -136,14 +139,18 @@ def _shape(x, w_gate, router_w):
 
 
 def make_args(x, router_w, w_gate, w_up, w_down, out, k: int, scales=None, route_idx=None,
-              route_gate=None) -> Args:
+              route_gate=None, activation: int = ACT_GELU, renormalize: bool = False,
+              capacity_factor: float = 0.0, norm_pre=None, norm_post=None, norm_eps: float = 1e-5) -> Args:
     T, d, f, E = _shape(x, w_gate, router_w)
     if tuple(w_up.shape) != (E, f, d) or tuple(w_down.shape) != (E, d, f):
         raise ValueError("w_up must be [E, f, d] and w_down [E, d, f]")
     if tuple(out.shape) != (T, d):
         raise ValueError("out must be [T, d]")
+    for name, g in (("norm_pre", norm_pre), ("norm_post", norm_post)):
+        if g is not None and (tuple(g.shape) != (d,) or g.dtype != x.dtype):
+            raise ValueError(f"{name} must be [d] = [{d}] of the activation dtype")
     _check_tensors(dict(x=x, router_w=router_w, w_gate=w_gate, w_up=w_up, w_down=w_down, out=out, scales=scales,
-                        route_idx=route_idx, route_gate=route_gate))
+                        route_idx=route_idx, route_gate=route_gate, norm_pre=norm_pre, norm_post=norm_post))
     a = Args()
     a.x, a.router_w, a.w_gate, a.w_up, a.w_down = _ptr(x), _ptr(router_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down)
     a.scales, a.out = _ptr(scales), _ptr(out)
@@ -151,6 +158,8 @@ def make_args(x, router_w, w_gate, w_up, w_down, out, k: int, scales=None, route
     a.act_dtype = _dtype_code(x)
     a.w_dtype = _dtype_code(w_gate)
     a.route_idx, a.route_gate = _ptr(route_idx), _ptr(route_gate)
+    a.activation, a.renormalize, a.capacity_factor = int(activation), int(bool(renormalize)), float(capacity_factor)
+    a.norm_pre, a.norm_post, a.norm_eps = _ptr(norm_pre), _ptr(norm_post), float(norm_eps)
     return a
 
 
@@ -200,15 +209,21 @@ def grok_moe_forward_f32(x, router_w, w_gate, w_up, w_down, out=None, k: int = 2
 
 def grok_moe_forward_ex(x, router_w, w_gate, w_up, w_down, k: int = 2, scales=None, out=None, workspace=None,
                         route_idx=None, route_gate=None, debug: bool = False,
-                        events: Optional[Sequence[object]] = None, stream=None):
+                        events: Optional[Sequence[object]] = None, stream=None, activation: int = ACT_GELU,
+                        renormalize: bool = False, capacity_factor: float = 0.0, norm_pre=None, norm_post=None,
+                        norm_eps: float = 1e-5):
     """Layer with caller workspace. Returns (out, dbg) where dbg holds the routing intermediates
-    (idx, gate, counts, offsets, perm, pos) as device tensors when debug=True, else {}.
-    `events`: up to 6 raw hipEvent_t handles (see `HipEvents`) recorded before each stage and after the last."""
+    (idx, gate, counts, offsets, perm, pos, and u with the sandwich norms) as device tensors when
+    debug=True, else {}.
+    `events`: up to 6 raw hipEvent_t handles (see `HipEvents`) recorded before each stage and after the last.
+    Variants: activation (ACT_GELU / ACT_SILU), renormalize, capacity_factor, norm_pre/norm_post/norm_eps
+    (the sandwich sub-layer out = x + RMSNorm(MoE(RMSNorm(x))))."""
     torch = _torch()
     dev = x.device
     if out is None:
         out = torch.empty_like(x)
-    a = make_args(x, router_w, w_gate, w_up, w_down, out, k, scales, route_idx, route_gate)
+    a = make_args(x, router_w, w_gate, w_up, w_down, out, k, scales, route_idx, route_gate, activation,
+                  renormalize, capacity_factor, norm_pre, norm_post, norm_eps)
     need = grok_moe_workspace_bytes(a.T, a.d, a.f, a.E, a.k, a.act_dtype, a.w_dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
@@ -224,6 +239,8 @@ def grok_moe_forward_ex(x, router_w, w_gate, w_up, w_down, k: int = 2, scales=No
                        offsets=torch.full((E + 1,), -7, dtype=torch.int32, device=dev),
                        perm=torch.full((T * k,), -7, dtype=torch.int32, device=dev),
                        pos=torch.full((T, k), -7, dtype=torch.int32, device=dev))
+            if norm_pre is not None:
+                dbg["u"] = torch.empty_like(x)
             for name, t in dbg.items():
                 setattr(d, name, t.data_ptr())
         if events:

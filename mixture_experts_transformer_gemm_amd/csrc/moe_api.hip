@@ -3,6 +3,7 @@
 #include "grok_moe.h"
 #include "moe_internal.h"
 
+#include <math.h>
 #include <string.h>
 
 using namespace gmoe;
@@ -23,7 +24,7 @@ struct Plan {
   int bm = 256;    // tiled path: rows per workgroup tile
   int64_t rows_cap = 0;
   size_t off_idx = 0, off_gate = 0, off_counts = 0, off_offsets = 0, off_perm = 0, off_pos = 0;
-  size_t off_H = 0, off_Y = 0, total = 0;
+  size_t off_U = 0, off_H = 0, off_Y = 0, total = 0;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -78,6 +79,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ac
   p.off_offsets = o; o = align256(o + sizeof(int32_t) * 65);
   p.off_perm = o;    o = align256(o + sizeof(int32_t) * (size_t)(T * k));
   p.off_pos = o;     o = align256(o + sizeof(int32_t) * (size_t)(T * k));
+  p.off_U = o;       o = align256(o + (act == GROK_MOE_F32 ? 4 : 2) * (size_t)T * (size_t)d);  // sandwich pre-norm
   p.off_H = o;       o = align256(o + hsz * (size_t)p.rows_cap * (size_t)f);
   p.off_Y = o;       o = align256(o + sizeof(float) * (size_t)p.splits * (size_t)p.rows_cap * (size_t)d);
   p.total = o;
@@ -97,8 +99,12 @@ int validate(const grok_moe_args* a) {
     return GROK_MOE_EINVAL;
   }
   if (a->w_dtype == GROK_MOE_I8 && !a->scales) return GROK_MOE_EINVAL;
+  if (a->activation != GROK_MOE_ACT_GELU && a->activation != GROK_MOE_ACT_SILU) return GROK_MOE_EINVAL;
+  if (!(a->capacity_factor >= 0.0) || !isfinite(a->capacity_factor)) return GROK_MOE_EINVAL;
+  if ((a->norm_pre == nullptr) != (a->norm_post == nullptr)) return GROK_MOE_EINVAL;
+  if (a->norm_pre && (!(a->norm_eps >= 0.0) || !isfinite(a->norm_eps))) return GROK_MOE_EINVAL;
   const void* ptrs[] = {a->x, a->router_w, a->w_gate, a->w_up, a->w_down, a->scales, a->out,
-                        a->route_idx, a->route_gate};
+                        a->route_idx, a->route_gate, a->norm_pre, a->norm_post};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return GROK_MOE_EALIGN;
   return GROK_MOE_OK;
@@ -112,6 +118,14 @@ int validate(const grok_moe_args* a) {
 int record(const grok_moe_debug* dbg, int i, hipStream_t st) {
   if (dbg && dbg->events[i]) return hipEventRecord((hipEvent_t)dbg->events[i], st) == hipSuccess;
   return 1;
+}
+
+// Rows each expert keeps under capacity factor c: floor(c * k * T / E), or -1
+// (no cap) for c == 0; at most k*T.
+int64_t capacity_rows(double c, int64_t T, int E, int k) {
+  if (!(c > 0.0)) return -1;
+  const double v = floor(c * (double)(k * T) / (double)E);
+  return v >= (double)(k * T) ? k * T : (int64_t)v;
 }
 
 int copy_out(void* dst, const void* src, size_t bytes, hipStream_t st) {
@@ -146,39 +160,48 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
   int32_t* offsets = (int32_t*)(w + p.off_offsets);
   int32_t* perm = (int32_t*)(w + p.off_perm);
   int32_t* pos = (int32_t*)(w + p.off_pos);
+  void* U = w + p.off_U;
   void* H = w + p.off_H;
   float* Y = (float*)(w + p.off_Y);
   const int64_t T = a->T;
   const int d = (int)a->d, f = (int)a->f, E = a->E, k = a->k;
   const int act_f32 = a->act_dtype == GROK_MOE_F32;
   const int w8 = a->w_dtype == GROK_MOE_I8;
+  const int sandwich = a->norm_pre != nullptr;
+  const int act = a->activation;
 
-  // stage 0: router
+  // stage 0: the sandwich pre-norm (the MoE input A is then u), router
   if (!record(dbg, 0, st)) return GROK_MOE_EHIP;
+  const void* A = a->x;
+  if (sandwich) {
+    GMOE_TRY(launch_rmsnorm(act_f32, a->x, a->norm_pre, T, d, a->norm_eps, U, st));
+    A = U;
+  }
   const int32_t* ridx = idx;
   const float* rgate = gate;
   if (a->route_idx) {
     ridx = a->route_idx;
     rgate = a->route_gate;
   } else {
-    GMOE_TRY(launch_router(act_f32, a->x, a->router_w, T, d, E, k, idx, gate, st));
+    GMOE_TRY(launch_router(act_f32, A, a->router_w, T, d, E, k, a->renormalize != 0, idx, gate, st));
   }
-  // stage 1: permutation
+  // stage 1: permutation (with the capacity cap)
   if (!record(dbg, 1, st)) return GROK_MOE_EHIP;
-  GMOE_TRY(launch_permute(ridx, T, E, k, counts, offsets, perm, pos, st));
+  GMOE_TRY(launch_permute(ridx, T, E, k, capacity_rows(a->capacity_factor, T, E, k), counts, offsets, perm, pos,
+                          st));
   const RouteView rv{counts, offsets, perm};
 
   // stage 2: gate/up projections + GELU * up
   if (!record(dbg, 2, st)) return GROK_MOE_EHIP;
   if (p.path == PATH_F32) {
-    GMOE_TRY(launch_f32_gateup((const float*)a->x, rv, (const float*)a->w_gate, (const float*)a->w_up, T,
-                               p.rows_cap, d, f, E, (float*)H, st));
+    GMOE_TRY(launch_f32_gateup((const float*)A, rv, (const float*)a->w_gate, (const float*)a->w_up, T,
+                               p.rows_cap, d, f, E, act, (float*)H, st));
   } else if (p.path == PATH_STREAM) {
-    GMOE_TRY(launch_stream_gateup(w8, p.mt_max, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, a->scales, T, d, f,
-                                  E, (bf16_bits*)H, st));
+    GMOE_TRY(launch_stream_gateup(w8, p.mt_max, (const bf16_bits*)A, rv, a->w_gate, a->w_up, a->scales, T, d, f, E,
+                                  act, (bf16_bits*)H, st));
   } else {
-    GMOE_TRY(launch_tiled_gateup(w8, p.bm, (const bf16_bits*)a->x, rv, a->w_gate, a->w_up, a->scales, T, p.rows_cap, d,
-                                 f, E, (bf16_bits*)H, st));
+    GMOE_TRY(launch_tiled_gateup(w8, p.bm, (const bf16_bits*)A, rv, a->w_gate, a->w_up, a->scales, T, p.rows_cap, d,
+                                 f, E, act, (bf16_bits*)H, st));
   }
   // stage 3: down projection
   if (!record(dbg, 3, st)) return GROK_MOE_EHIP;
@@ -193,14 +216,20 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
   }
   // stage 4: gate-weighted combine
   if (!record(dbg, 4, st)) return GROK_MOE_EHIP;
-  GMOE_TRY(launch_combine(act_f32, Y, p.splits, p.rows_cap, pos, rgate, T, d, k, a->out, st));
+  if (sandwich) {
+    GMOE_TRY(launch_combine_sandwich(act_f32, Y, p.splits, p.rows_cap, pos, rgate, T, d, k, a->x, a->norm_post,
+                                     a->norm_eps, a->out, st));
+  } else {
+    GMOE_TRY(launch_combine(act_f32, Y, p.splits, p.rows_cap, pos, rgate, T, d, k, a->out, st));
+  }
   if (!record(dbg, 5, st)) return GROK_MOE_EHIP;
 
   if (dbg) {
     const size_t tk = (size_t)(T * k);
     if (!copy_out(dbg->idx, ridx, 4 * tk, st) || !copy_out(dbg->gate, rgate, 4 * tk, st) ||
         !copy_out(dbg->counts, counts, 4 * (size_t)E, st) || !copy_out(dbg->offsets, offsets, 4 * (size_t)(E + 1), st) ||
-        !copy_out(dbg->perm, perm, 4 * tk, st) || !copy_out(dbg->pos, pos, 4 * tk, st))
+        !copy_out(dbg->perm, perm, 4 * tk, st) || !copy_out(dbg->pos, pos, 4 * tk, st) ||
+        (sandwich && !copy_out(dbg->u, U, (act_f32 ? 4 : 2) * (size_t)T * (size_t)d, st)))
       return GROK_MOE_EHIP;
   }
   return GROK_MOE_OK;

@@ -23,7 +23,7 @@ __device__ __forceinline__ int expert_of_row(const RouteView& rv, int E, int row
 __global__ __launch_bounds__(256) void f32_gateup_kernel(const float* __restrict__ x, RouteView rv,
                                                          const float* __restrict__ wg,
                                                          const float* __restrict__ wu, int64_t T,
-                                                         int64_t rows_cap, int d, int f, int E,
+                                                         int64_t rows_cap, int d, int f, int E, int act,
                                                          float* __restrict__ H) {
   const int64_t total = rows_cap * f;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void f32_gateup_kernel(const float* __restrict
       a = fmaf(xv.x, gv.x, a); a = fmaf(xv.y, gv.y, a); a = fmaf(xv.z, gv.z, a); a = fmaf(xv.w, gv.w, a);
       b = fmaf(xv.x, uv.x, b); b = fmaf(xv.y, uv.y, b); b = fmaf(xv.z, uv.z, b); b = fmaf(xv.w, uv.w, b);
     }
-    H[(int64_t)row * f + n] = gelu_erf(a) * b;
+    H[(int64_t)row * f + n] = glu_act(act, a) * b;
   }
 }
 
@@ -70,12 +70,12 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__
 }
 
 hipError_t launch_f32_gateup(const float* x, RouteView rv, const float* wg, const float* wu, int64_t T,
-                             int64_t rows_cap, int d, int f, int E, float* H, hipStream_t st) {
+                             int64_t rows_cap, int d, int f, int E, int act, float* H, hipStream_t st) {
   int64_t blocks = (rows_cap * f + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(f32_gateup_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, rv, wg, wu, T, rows_cap, d,
-                     f, E, H);
+                     f, E, act, H);
   return hipGetLastError();
 }
 

@@ -30,6 +30,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Exact-erf GELU: z * Phi(z) = z (1 + erf(z / sqrt 2)) / 2, with the device library's erff.
 __device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
 
+// SiLU: z * sigmoid(z) = z / (1 + e^-z), with the device library's expf (z -> -inf gives -0).
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Activation of the gate branch: ACT_GELU (Grok-1's GeGLU experts) or ACT_SILU
+// (SwiGLU experts). The flag is uniform over a launch.
+enum { ACT_GELU = 0, ACT_SILU = 1 };
+__device__ __forceinline__ float glu_act(int act, float z) { return act == ACT_SILU ? silu(z) : gelu_erf(z); }
+
 // Device view of the routing produced by the permutation stage.
 struct RouteView {
   const int32_t* counts;   // [E] rows per expert
@@ -40,22 +48,36 @@ struct RouteView {
 // ---------------------------------------------------------------- launchers
 // All launchers enqueue on `stream` and return the launch status.
 
+// renorm: divide the k selected gates by their sum.
 hipError_t launch_router(int act_f32, const void* x, const void* router_w, int64_t T, int d, int E, int k,
-                         int32_t* idx, float* gate, hipStream_t stream);
+                         int renorm, int32_t* idx, float* gate, hipStream_t stream);
 
-hipError_t launch_permute(const int32_t* idx, int64_t T, int E, int k, int32_t* counts, int32_t* offsets,
-                          int32_t* perm, int32_t* pos, hipStream_t stream);
+// cap >= 0: an expert keeps its first `cap` assignments in token order, the
+// others get pos = -1 and no row; cap < 0: no cap.
+hipError_t launch_permute(const int32_t* idx, int64_t T, int E, int k, int64_t cap, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t stream);
 
 // out[t] = sum_s gate[t][s] * (sum_{p<S} Y[p][pos[t][s]]), Y: [S][rows_cap][d] fp32
 hipError_t launch_combine(int out_f32, const float* Y, int S, int64_t rows_cap, const int32_t* pos,
                           const float* gate, int64_t T, int d, int k, void* out, hipStream_t stream);
 
+// u[t] = RMSNorm(x[t]; g, eps), computed in fp64 and rounded once to the
+// activation type (bf16 RNE, or fp32).
+hipError_t launch_rmsnorm(int act_f32, const void* x, const void* g, int64_t T, int d, double eps, void* u,
+                          hipStream_t stream);
+
+// Sandwich epilogue: y[t] = the gated sum of combine (fp32), then
+// out[t] = x[t] + RMSNorm(y[t]; g_post, eps), one rounding to the output type.
+hipError_t launch_combine_sandwich(int out_f32, const float* Y, int S, int64_t rows_cap, const int32_t* pos,
+                                   const float* gate, int64_t T, int d, int k, const void* x, const void* g_post,
+                                   double eps, void* out, hipStream_t stream);
+
 // Weight-streaming path: bf16 weights with every expert segment <= max_rows
 // <= 64 rows, or 8-bit weights (w8, scales) with segments processed in
 // chunks of up to 128 rows.
 hipError_t launch_stream_gateup(int w8, int max_rows, const bf16_bits* x, RouteView rv, const void* wg,
-                                const void* wu, const float* scales, int64_t T, int d, int f, int E, bf16_bits* H,
-                                hipStream_t stream);
+                                const void* wu, const float* scales, int64_t T, int d, int f, int E, int act,
+                                bf16_bits* H, hipStream_t stream);
 hipError_t launch_stream_down(int w8, int max_rows, int splits, const bf16_bits* H, RouteView rv, const void* wd,
                               const float* scales, int64_t rows_cap, int d, int f, int E, float* Y,
                               hipStream_t stream);
@@ -63,7 +85,7 @@ hipError_t launch_stream_down(int w8, int max_rows, int splits, const bf16_bits*
 // Large-M path (LDS-tiled MFMA grouped GEMM).
 // bm: rows per workgroup tile (64, 128 or 256).
 hipError_t launch_tiled_gateup(int w8, int bm, const bf16_bits* x, RouteView rv, const void* wg, const void* wu,
-                               const float* scales, int64_t T, int64_t rows_cap, int d, int f, int E,
+                               const float* scales, int64_t T, int64_t rows_cap, int d, int f, int E, int act,
                                bf16_bits* H, hipStream_t stream);
 // splits: partial sums over equal slices of the reduction (Y holds `splits` of them).
 hipError_t launch_tiled_down(int w8, int bm, int splits, const bf16_bits* H, RouteView rv, const void* wd,
@@ -72,7 +94,7 @@ hipError_t launch_tiled_down(int w8, int bm, int splits, const bf16_bits* H, Rou
 
 // fp32 path (plain FMA kernels, fp32 accumulation).
 hipError_t launch_f32_gateup(const float* x, RouteView rv, const float* wg, const float* wu, int64_t T,
-                             int64_t rows_cap, int d, int f, int E, float* H, hipStream_t stream);
+                             int64_t rows_cap, int d, int f, int E, int act, float* H, hipStream_t stream);
 hipError_t launch_f32_down(const float* H, RouteView rv, const float* wd, int64_t rows_cap, int d, int f, int E,
                            float* Y, hipStream_t stream);
 

@@ -104,7 +104,8 @@ template <bool GATEUP, int MT, bool W8>
 __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __restrict__ A, RouteView rv,
                                                           const void* __restrict__ w0, const void* __restrict__ w1,
                                                           const float* __restrict__ scales, int64_t T, int K,
-                                                          int N, int E, int64_t rows_cap, void* __restrict__ out) {
+                                                          int N, int E, int64_t rows_cap, int act,
+                                                          void* __restrict__ out) {
   using C = BsCfg<MT, W8>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
               gt *= scales[(int64_t)e * N + c0 + 4 * g + v];
               u *= scales[(int64_t)E * N + (int64_t)e * N + c0 + 4 * g + v];
             }
-            h[v] = gelu_erf(gt) * u;
+            h[v] = glu_act(act, gt) * u;
           }
           uint2 o;
           o.x = pack_bf16x2(h[0], h[1]);
@@ -297,13 +298,13 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
 template <bool GATEUP, int MT, bool W8>
 static hipError_t stream_launch(dim3 grid, hipStream_t st, const bf16_bits* A, RouteView rv, const void* w0,
                                 const void* w1, const float* scales, int64_t T, int K, int N, int E,
-                                int64_t rows_cap, void* out) {
+                                int64_t rows_cap, int act, void* out) {
   constexpr int lds = BsCfg<MT, W8>::kLdsBytes;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&stream_kernel<GATEUP, MT, W8>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((stream_kernel<GATEUP, MT, W8>), grid, dim3(kBW * 64), lds, st, A, rv, w0, w1, scales, T, K,
-                     N, E, rows_cap, out);
+                     N, E, rows_cap, act, out);
   return hipGetLastError();
 }
 
@@ -311,25 +312,25 @@ static hipError_t stream_launch(dim3 grid, hipStream_t st, const bf16_bits* A, R
 template <bool GATEUP, bool W8>
 static hipError_t stream_dispatch(int max_rows, unsigned gx, unsigned gy, hipStream_t st, const bf16_bits* A,
                                   RouteView rv, const void* w0, const void* w1, const float* scales, int64_t T,
-                                  int K, int N, int E, int64_t rows_cap, void* out) {
+                                  int K, int N, int E, int64_t rows_cap, int act, void* out) {
   auto chunks = [&](int xr) { return (unsigned)((max_rows + xr - 1) / xr); };
   if (max_rows <= 16)
-    return stream_launch<GATEUP, 1, W8>(dim3(gx, gy, 1), st, A, rv, w0, w1, scales, T, K, N, E, rows_cap, out);
+    return stream_launch<GATEUP, 1, W8>(dim3(gx, gy, 1), st, A, rv, w0, w1, scales, T, K, N, E, rows_cap, act, out);
   if (max_rows <= 32)
-    return stream_launch<GATEUP, 2, W8>(dim3(gx, gy, 1), st, A, rv, w0, w1, scales, T, K, N, E, rows_cap, out);
+    return stream_launch<GATEUP, 2, W8>(dim3(gx, gy, 1), st, A, rv, w0, w1, scales, T, K, N, E, rows_cap, act, out);
   if (max_rows <= 64 || !W8)
     return stream_launch<GATEUP, 4, W8>(dim3(gx, gy, chunks(64)), st, A, rv, w0, w1, scales, T, K, N, E, rows_cap,
-                                        out);
+                                        act, out);
   return stream_launch<GATEUP, 8, W8>(dim3(gx, gy, chunks(128)), st, A, rv, w0, w1, scales, T, K, N, E, rows_cap,
-                                      out);
+                                      act, out);
 }
 
 hipError_t launch_stream_gateup(int w8, int max_rows, const bf16_bits* x, RouteView rv, const void* wg,
-                                const void* wu, const float* scales, int64_t T, int d, int f, int E, bf16_bits* H,
-                                hipStream_t st) {
+                                const void* wu, const float* scales, int64_t T, int d, int f, int E, int act,
+                                bf16_bits* H, hipStream_t st) {
   const unsigned gx = (unsigned)E * (unsigned)(f / (kBW * 8));
-  return w8 ? stream_dispatch<true, true>(max_rows, gx, 1u, st, x, rv, wg, wu, scales, T, d, f, E, 0, H)
-            : stream_dispatch<true, false>(max_rows, gx, 1u, st, x, rv, wg, wu, scales, T, d, f, E, 0, H);
+  return w8 ? stream_dispatch<true, true>(max_rows, gx, 1u, st, x, rv, wg, wu, scales, T, d, f, E, 0, act, H)
+            : stream_dispatch<true, false>(max_rows, gx, 1u, st, x, rv, wg, wu, scales, T, d, f, E, 0, act, H);
 }
 
 hipError_t launch_stream_down(int w8, int max_rows, int splits, const bf16_bits* H, RouteView rv, const void* wd,
@@ -337,9 +338,9 @@ hipError_t launch_stream_down(int w8, int max_rows, int splits, const bf16_bits*
                               hipStream_t st) {
   const unsigned gx = (unsigned)E * (unsigned)(d / (kBW * 16));
   return w8 ? stream_dispatch<false, true>(max_rows, gx, (unsigned)splits, st, H, rv, wd, wd, scales, 0, f, d, E,
-                                           rows_cap, Y)
+                                           rows_cap, 0, Y)
             : stream_dispatch<false, false>(max_rows, gx, (unsigned)splits, st, H, rv, wd, wd, scales, 0, f, d, E,
-                                            rows_cap, Y);
+                                            rows_cap, 0, Y);
 }
 
 }  // namespace gmoe

@@ -111,7 +111,7 @@ __device__ __forceinline__ const char* weight_row(const void* w0, const void* w1
 // GELU(gate) * up (gate/up pass, bf16 H) or stores the fp32 down product.
 template <int BM, bool GATEUP, bool W8, int NW = 4>
 __device__ __forceinline__ void epilogue(AccT<BM, NW>& acc, const Tile& t,
-                                         const float* __restrict__ scales, int N, int E, int Ftot,
+                                         const float* __restrict__ scales, int N, int E, int Ftot, int act,
                                          void* __restrict__ out) {
   using C = TileCfg<BM, NW>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -138,7 +138,7 @@ __device__ __forceinline__ void epilogue(AccT<BM, NW>& acc, const Tile& t,
             float h[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-              h[v] = gelu_erf(acc[i][j][4 * q + v] * s0[v]) * (acc[i + C::TI / 2][j][4 * q + v] * s1[v]);
+              h[v] = glu_act(act, acc[i][j][4 * q + v] * s0[v]) * (acc[i + C::TI / 2][j][4 * q + v] * s1[v]);
             uint2 o;
             o.x = pack_bf16x2(h[0], h[1]);
             o.y = pack_bf16x2(h[2], h[3]);
@@ -252,7 +252,8 @@ template <int BM, bool GATEUP, int NW, int NS, bool W8>
 __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __restrict__ A, RouteView rv,
                                                      const void* __restrict__ w0, const void* __restrict__ w1,
                                                      const float* __restrict__ scales, int64_t T, int K, int N,
-                                                     int E, int Ftot, int64_t rows_cap, void* __restrict__ out) {
+                                                     int E, int Ftot, int64_t rows_cap, int act,
+                                                     void* __restrict__ out) {
   using C = TileCfg<BM, NW>;
   using D = DmaCfg<BM, NW, NS, W8>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -421,7 +422,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
   }
   // drain the (duplicate) loads still in flight before the workgroup exits
   GMOE_WAIT_VM_LGKM0(0);
-  epilogue<BM, GATEUP, W8, NW>(acc, t, scales, N, E, Ftot, out);
+  epilogue<BM, GATEUP, W8, NW>(acc, t, scales, N, E, Ftot, act, out);
 }
 
 // =====================================================================
@@ -447,7 +448,7 @@ struct DmaChoice {
 template <int BM, bool GATEUP, bool W8>
 static hipError_t launch_dma(hipStream_t st, const bf16_bits* A, RouteView rv, const void* w0, const void* w1,
                              const float* scales, int64_t T, int64_t rows_cap, int K, int N, int E, int Ftot,
-                             int splits, void* out) {
+                             int splits, int act, void* out) {
   using P = DmaChoice<BM, W8>;
   constexpr int lds = DmaCfg<BM, P::NW, P::NS, W8>::kLdsBytes;
   static const hipError_t attr =
@@ -456,41 +457,41 @@ static hipError_t launch_dma(hipStream_t st, const bf16_bits* A, RouteView rv, c
   if (attr != hipSuccess) return attr;
   const dim3 grid(tiled_blocks(BM, rows_cap, E, N / (GATEUP ? TBN / 2 : TBN)), (unsigned)splits);
   hipLaunchKernelGGL((dma_kernel<BM, GATEUP, P::NW, P::NS, W8>), grid, dim3(P::NW * 64), lds, st, A, rv, w0, w1,
-                     scales, T, K, N, E, Ftot, rows_cap, out);
+                     scales, T, K, N, E, Ftot, rows_cap, act, out);
   return hipGetLastError();
 }
 
 template <int BM, bool GATEUP>
 static hipError_t tiled_launch(bool w8, hipStream_t st, const bf16_bits* A, RouteView rv, const void* w0,
                                const void* w1, const float* scales, int64_t T, int64_t rows_cap, int K, int N, int E,
-                               int Ftot, int splits, void* out) {
-  return w8 ? launch_dma<BM, GATEUP, true>(st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, out)
-            : launch_dma<BM, GATEUP, false>(st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, out);
+                               int Ftot, int splits, int act, void* out) {
+  return w8 ? launch_dma<BM, GATEUP, true>(st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, act, out)
+            : launch_dma<BM, GATEUP, false>(st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, act, out);
 }
 
 template <bool GATEUP>
 static hipError_t tiled_dispatch(bool w8, int bm, hipStream_t st, const bf16_bits* A, RouteView rv, const void* w0,
                                  const void* w1, const float* scales, int64_t T, int64_t rows_cap, int K, int N,
-                                 int E, int Ftot, int splits, void* out) {
+                                 int E, int Ftot, int splits, int act, void* out) {
   switch (bm) {
-    case 64: return tiled_launch<64, GATEUP>(w8, st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, out);
+    case 64: return tiled_launch<64, GATEUP>(w8, st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, act, out);
     case 128:
-      return tiled_launch<128, GATEUP>(w8, st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, out);
+      return tiled_launch<128, GATEUP>(w8, st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, act, out);
     case 256:
-      return tiled_launch<256, GATEUP>(w8, st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, out);
+      return tiled_launch<256, GATEUP>(w8, st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, act, out);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_tiled_gateup(int w8, int bm, const bf16_bits* x, RouteView rv, const void* wg, const void* wu,
-                               const float* scales, int64_t T, int64_t rows_cap, int d, int f, int E,
+                               const float* scales, int64_t T, int64_t rows_cap, int d, int f, int E, int act,
                                bf16_bits* H, hipStream_t st) {
-  return tiled_dispatch<true>(w8 != 0, bm, st, x, rv, wg, wu, scales, T, rows_cap, d, f, E, f, 1, H);
+  return tiled_dispatch<true>(w8 != 0, bm, st, x, rv, wg, wu, scales, T, rows_cap, d, f, E, f, 1, act, H);
 }
 
 hipError_t launch_tiled_down(int w8, int bm, int splits, const bf16_bits* H, RouteView rv, const void* wd,
                              const float* scales, int64_t rows_cap, int d, int f, int E, float* Y, hipStream_t st) {
-  return tiled_dispatch<false>(w8 != 0, bm, st, H, rv, wd, wd, scales, rows_cap, rows_cap, f, d, E, f, splits, Y);
+  return tiled_dispatch<false>(w8 != 0, bm, st, H, rv, wd, wd, scales, rows_cap, rows_cap, f, d, E, f, splits, 0, Y);
 }
 
 }  // namespace gmoe

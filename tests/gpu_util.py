@@ -21,19 +21,27 @@ def to_dev(a, torch):
 
 
 def dev_workload(w: synthetic.Workload, torch):
-    return {n: to_dev(getattr(w, n), torch) for n in ("x", "router_w", "w_gate", "w_up", "w_down", "scales")}
+    return {n: to_dev(getattr(w, n), torch)
+            for n in ("x", "router_w", "w_gate", "w_up", "w_down", "scales", "norm_pre", "norm_post")}
 
 
 def run_layer(w: synthetic.Workload, torch, dev=None, route_idx=None, route_gate=None, debug=True):
-    """One layer call via grok_moe_forward_ex. Returns (out f64 [T,d], dbg numpy dict)."""
+    """One layer call via grok_moe_forward_ex, with the workload's variant knobs.
+    Returns (out f64 [T,d], dbg numpy dict; bf16 tensors as uint16 bits)."""
     dev = dev or dev_workload(w, torch)
     ri = None if route_idx is None else torch.from_numpy(np.ascontiguousarray(route_idx, np.int32)).cuda()
     rg = None if route_gate is None else torch.from_numpy(np.ascontiguousarray(route_gate, np.float32)).cuda()
     out, dbg = gm.grok_moe_forward_ex(dev["x"], dev["router_w"], dev["w_gate"], dev["w_up"], dev["w_down"],
-                                      k=w.k, scales=dev["scales"], route_idx=ri, route_gate=rg, debug=debug)
+                                      k=w.k, scales=dev["scales"], route_idx=ri, route_gate=rg, debug=debug,
+                                      activation=gm.ACT_SILU if w.activation == "silu" else gm.ACT_GELU,
+                                      renormalize=w.renormalize, capacity_factor=w.capacity_factor,
+                                      norm_pre=dev["norm_pre"], norm_post=dev["norm_post"], norm_eps=w.norm_eps)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy().astype(np.float64)
-    return got, {n: t.cpu().numpy() for n, t in dbg.items()}
+    host = {}
+    for n, t in dbg.items():
+        host[n] = t.view(torch.int16).cpu().numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.cpu().numpy()
+    return got, host
 
 
 def normwise_err(got: np.ndarray, ref: np.ndarray) -> float:

@@ -46,9 +46,9 @@ def test_workspace_bytes():
     # decode shape: idx/gate/perm/pos + H [16, f] bf16 + split-K Y partials
     ws = gm.grok_moe_workspace_bytes(8, 6144, 32768, 8, 2)
     assert ws >= 16 * 32768 * 2 + 16 * 6144 * 4
-    # prefill: H [16384, 32768] bf16 dominates
+    # prefill: H [16384, 32768] bf16 dominates; Y [16384, 6144] fp32; u [8192, 6144] bf16 for the sandwich norms
     ws = gm.grok_moe_workspace_bytes(8192, 6144, 32768, 8, 2)
-    assert 16384 * 32768 * 2 <= ws < 16384 * 32768 * 2 + 16384 * 6144 * 4 + (1 << 20)
+    assert 16384 * 32768 * 2 <= ws < 16384 * 32768 * 2 + 16384 * 6144 * 4 + 8192 * 6144 * 2 + (1 << 20)
     assert gm.grok_moe_workspace_bytes(0, 6144, 32768, 8, 2) > 0
     # invalid / unsupported shapes report 0
     assert gm.grok_moe_workspace_bytes(8, 6144, 32768, 8, 9) == 0          # k > E
@@ -61,7 +61,8 @@ def _args(**kw):
     a = gm.Args()
     base = dict(x=0x10000, router_w=0x20000, w_gate=0x30000, w_up=0x40000, w_down=0x50000, scales=None,
                 out=0x60000, T=8, d=256, f=512, E=8, k=2, act_dtype=gm.BF16, w_dtype=gm.BF16, route_idx=None,
-                route_gate=None)
+                route_gate=None, activation=gm.ACT_GELU, renormalize=0, capacity_factor=0.0, norm_pre=None,
+                norm_post=None, norm_eps=1e-5)
     base.update(kw)
     for n, v in base.items():
         setattr(a, n, v)
@@ -95,9 +96,51 @@ def _call(a, ws=0x1000000, ws_bytes=1 << 40):
     (dict(x=0x10008), gm.EALIGN),
     (dict(w_up=0x40004), gm.EALIGN),
     (dict(out=0x60002), gm.EALIGN),
+    # variants
+    (dict(activation=2), gm.EINVAL),
+    (dict(activation=-1), gm.EINVAL),
+    (dict(capacity_factor=-0.5), gm.EINVAL),
+    (dict(capacity_factor=float("nan")), gm.EINVAL),
+    (dict(capacity_factor=float("inf")), gm.EINVAL),
+    (dict(norm_pre=0x80000), gm.EINVAL),              # one norm without the other
+    (dict(norm_post=0x90000), gm.EINVAL),
+    (dict(norm_pre=0x80000, norm_post=0x90000, norm_eps=-1e-5), gm.EINVAL),
+    (dict(norm_pre=0x80000, norm_post=0x90000, norm_eps=float("nan")), gm.EINVAL),
+    (dict(norm_pre=0x80008, norm_post=0x90000), gm.EALIGN),
 ])
 def test_validation_errors(kw, code):
     assert _call(_args(**kw)) == code
+
+
+def test_variant_arguments_reach_the_workspace_check():
+    # valid variant knobs pass validation (the call then stops at the missing workspace)
+    for kw in (dict(activation=gm.ACT_SILU, renormalize=1), dict(capacity_factor=1.25),
+               dict(norm_pre=0x80000, norm_post=0x90000, norm_eps=0.0)):
+        assert _call(_args(**kw), ws=0, ws_bytes=0) == gm.EWORKSPACE
+
+
+def test_ctypes_structs_match_the_header(tmp_path):
+    # offsets and sizes of grok_moe_args / grok_moe_debug as the C compiler lays them out
+    fields = {"grok_moe_args": gm.Args, "grok_moe_debug": gm.Debug}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "grok_moe.h"', "int main(void) {"]
+    for cname, py in fields.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.check_call(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)])
+    got = {}
+    for line in subprocess.check_output([str(exe)], text=True).splitlines():
+        cname, fname, val = line.split()
+        got[(cname, fname)] = int(val)
+    for cname, py in fields.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
 
 
 def test_workspace_errors():

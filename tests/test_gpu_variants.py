@@ -1,0 +1,196 @@
+"""GPU parity of the layer variants against the CPU oracle (``oracle.layer``):
+SiLU experts with renormalised gates (the Mixtral variant), capacity-factor
+drops, and the sandwich sub-layer (RMSNorm before and after the MoE, plus the
+residual), on the bf16, 8-bit and fp32 paths, small shapes spanning the
+weight-streaming and tiled kernels, and at full Mixtral 8x22B / Grok-1 sizes.
+
+Rules as in the other parity tests: routing indices equal the oracle's; the
+permutation (with dropped assignments at pos = -1) is bit-exact against the
+oracle's capped permutation of the GPU routing; the pre-norm output u is
+bit-exact against the oracle's bf16 rounding; outputs are within the per-token
+normwise tolerance (2e-2 bf16, 5e-2 8-bit, 1e-4 fp32).
+"""
+import gc
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from gpu_util import TOL, TIE_WINDOW, dev_workload, normwise_err, run_layer
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(w, tokens=None):
+    return oracle.layer(w.x, w.router_w, w.w_gate, w.w_up, w.w_down, w.k, scales=w.scales,
+                        activation=oracle.SILU if w.activation == "silu" else oracle.GELU,
+                        renormalize=w.renormalize, capacity_factor=w.capacity_factor, norm_pre=w.norm_pre,
+                        norm_post=w.norm_post, norm_eps=w.norm_eps, tokens=tokens)
+
+
+def _tol(w):
+    return TOL["f32" if w.act_dtype == "f32" else ("i8" if w.w_dtype == "i8" else "bf16")]
+
+
+def _check(w, tokens=None, label=""):
+    print(f"[variants] {label} T={w.T} d={w.d} f={w.f} E={w.E} k={w.k} act={w.activation} "
+          f"renorm={w.renormalize} cap={w.capacity_factor} sandwich={w.norm_pre is not None} "
+          f"w={w.w_dtype}", flush=True)
+    got, dbg = run_layer(w, torch)
+    ref = _oracle(w, tokens=tokens)
+    if w.norm_pre is not None:
+        np.testing.assert_array_equal(dbg["u"], ref["u"])          # pre-norm output, bit-exact
+    np.testing.assert_array_equal(dbg["idx"], ref["idx"])          # routing decided on u, fp64 logits
+    gate_tol = 1e-6 * np.maximum(ref["gate"], 1e-30) + 1e-12
+    assert np.all(np.abs(dbg["gate"].astype(np.float64) - ref["gate"]) <= gate_tol)
+    if w.renormalize:
+        np.testing.assert_allclose(dbg["gate"].sum(axis=1), 1.0, atol=1e-6)
+    cap = oracle.capacity(w.capacity_factor, w.T, w.E, w.k)
+    c, o, p, pos = oracle.permute_cap(dbg["idx"], w.E, cap)
+    np.testing.assert_array_equal(dbg["counts"], c)
+    np.testing.assert_array_equal(dbg["offsets"], o)
+    np.testing.assert_array_equal(dbg["perm"][:o[-1]], p[:o[-1]])
+    np.testing.assert_array_equal(dbg["pos"], pos)
+    np.testing.assert_array_equal(dbg["pos"], ref["pos"])
+    sub = got if tokens is None else got[tokens]
+    err = normwise_err(sub, ref["out"])
+    print(f"[variants] {label}: normwise error {err:.3e} (tol {_tol(w)})", flush=True)
+    assert np.all(np.isfinite(got))
+    assert err <= _tol(w), f"normwise error {err:.3e}"
+    return got, dbg, ref
+
+
+# ---------------------------------------------------------------- SiLU + renormalised gates (Mixtral)
+@pytest.mark.parametrize("T", [1, 5, 64, 100, 300, 777])
+def test_mixtral_variant_bf16(T):
+    w = synthetic.make("mixtral_decode", T=T, d=256, f=512, seed=200 + T)
+    _check(w, label="mixtral bf16")
+
+
+@pytest.mark.parametrize("T", [40, 513])
+def test_silu_int8(T):
+    w = synthetic.make("int8", T=T, d=256, f=512, seed=T, activation="silu", renormalize=True)
+    w.scales = synthetic.random_scales(w.E, w.d, w.f, seed=T)
+    _check(w, label="silu int8")
+
+
+def test_silu_f32():
+    w = synthetic.make("tiny_f32", activation="silu", renormalize=True)
+    _check(w, label="silu f32")
+
+
+def test_renormalised_zero_router():
+    w = synthetic.make("mixtral_decode", T=30, d=256, f=256, seed=3)
+    w.router_w[:] = 0
+    got, dbg, _ = _check(w, label="renorm zero router")
+    assert np.all(dbg["idx"] == [0, 1]) and np.all(dbg["gate"] == np.float32(0.5))
+
+
+# ---------------------------------------------------------------- capacity
+@pytest.mark.parametrize("T,cf", [(40, 0.5), (64, 1.0), (300, 1.0), (777, 0.75), (1600, 1.25)])
+def test_capacity_skewed_bf16(T, cf):
+    w = synthetic.make("skew", T=T, d=256, f=512, seed=T, capacity_factor=cf)
+    got, dbg, ref = _check(w, label="capacity")
+    assert (dbg["pos"] == -1).any(), "the skewed routing must overflow"
+    assert dbg["counts"].max() <= oracle.capacity(cf, T, w.E, w.k)
+
+
+def test_capacity_int8():
+    w = synthetic.make("skew", T=200, d=256, f=512, seed=5, w_dtype="i8", capacity_factor=0.8)
+    _check(w, label="capacity int8")
+
+
+def test_capacity_zero_rows_gives_zero_output():
+    w = synthetic.make("decode", T=50, d=256, f=256, seed=6, capacity_factor=1e-3)
+    got, dbg, _ = _check(w, label="capacity 0 rows")
+    assert (dbg["pos"] == -1).all() and (dbg["counts"] == 0).all()
+    assert (got == 0.0).all()
+
+
+# ---------------------------------------------------------------- sandwich sub-layer
+@pytest.mark.parametrize("T", [1, 8, 64, 300])
+def test_sandwich_bf16(T):
+    w = synthetic.make("decode", T=T, d=256, f=512, seed=300 + T, sandwich=True)
+    _check(w, label="sandwich bf16")
+
+
+def test_sandwich_f32_and_int8():
+    _check(synthetic.make("tiny_f32", sandwich=True), label="sandwich f32")
+    w = synthetic.make("int8", T=40, d=256, f=512, seed=4, sandwich=True)
+    _check(w, label="sandwich int8")
+
+
+def test_sandwich_zero_experts_is_the_residual():
+    w = synthetic.make("decode", T=70, d=256, f=256, seed=7, sandwich=True)
+    w.w_down = np.zeros_like(w.w_down)
+    got, _, _ = _check(w, label="sandwich zero experts")
+    np.testing.assert_array_equal(got, synthetic.bf16_bits_to_f32(w.x).astype(np.float64))
+
+
+def test_all_variants_together():
+    w = synthetic.make("skew", T=200, d=256, f=512, seed=8, activation="silu", renormalize=True,
+                       capacity_factor=0.9, sandwich=True)
+    got, dbg, _ = _check(w, label="all variants")
+    dropped = np.all(dbg["pos"] == -1, axis=1)
+    if dropped.any():   # tokens whose every assignment overflowed carry the residual only
+        np.testing.assert_array_equal(got[dropped], synthetic.bf16_bits_to_f32(w.x[dropped]).astype(np.float64))
+
+
+def test_variants_deterministic_bitwise():
+    w = synthetic.make("skew", T=300, d=256, f=512, seed=9, activation="silu", renormalize=True,
+                       capacity_factor=0.9, sandwich=True)
+    dev = dev_workload(w, torch)
+    a, da = run_layer(w, torch, dev=dev)
+    b, db = run_layer(w, torch, dev=dev)
+    np.testing.assert_array_equal(a, b)
+    for n in da:
+        np.testing.assert_array_equal(da[n], db[n])
+
+
+# ---------------------------------------------------------------- full sizes
+def _sample(dbg, E, T, n_random, seed):
+    offs, perm = dbg["offsets"], dbg["perm"]
+    pick = []
+    for e in range(E):
+        if offs[e + 1] > offs[e]:
+            pick += [int(perm[offs[e]]), int(perm[offs[e + 1] - 1])]
+    pick += list(np.random.default_rng(seed).choice(T, size=min(n_random, T), replace=False))
+    return sorted(set(pick))
+
+
+def test_mixtral_decode_full():
+    # Mixtral 8x22B expert shapes (d=6144, f=16384), SiLU, renormalised gates, 8 tokens, all checked
+    w = synthetic.make("mixtral_decode")
+    _check(w, label="mixtral decode full")
+    del w
+    gc.collect()
+
+
+def test_sandwich_decode_full():
+    w = synthetic.make("decode", sandwich=True)
+    _check(w, label="sandwich decode full")
+    del w
+    gc.collect()
+
+
+def test_capacity_skew_full_sampled():
+    # full Grok-1 shapes at the skewed 2048-token workload with capacity factor 1.0:
+    # experts 0 and 1 overflow; routing/permutation for all tokens, outputs on a sample
+    w = synthetic.make("skew", capacity_factor=1.0)
+    got, dbg = run_layer(w, torch)
+    ref_all = _oracle(w, tokens=[0])                 # routing + capped permutation of every token
+    np.testing.assert_array_equal(dbg["idx"], ref_all["idx"])
+    np.testing.assert_array_equal(dbg["pos"], ref_all["pos"])
+    assert dbg["counts"][0] == oracle.capacity(1.0, w.T, w.E, w.k) == 512
+    toks = _sample(dbg, w.E, w.T, 6, seed=1)
+    dropped = [t for t in range(w.T) if (dbg["pos"][t] == -1).all()][:2]
+    toks = sorted(set(toks + dropped))
+    ref = _oracle(w, tokens=toks)
+    err = normwise_err(got[toks], ref["out"])
+    print(f"[variants] capacity skew full: {len(toks)} tokens, normwise error {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+    del w
+    gc.collect()
