@@ -43,7 +43,8 @@ class _Layer(ctypes.Structure):
                 ("scales", ctypes.c_void_p), ("T", ctypes.c_int64), ("d", ctypes.c_int64), ("f", ctypes.c_int64),
                 ("E", ctypes.c_int), ("k", ctypes.c_int), ("act", ctypes.c_int), ("renormalize", ctypes.c_int),
                 ("capacity_factor", ctypes.c_double), ("norm_pre", ctypes.c_void_p),
-                ("norm_post", ctypes.c_void_p), ("norm_dt", ctypes.c_int), ("norm_eps", ctypes.c_double)]
+                ("norm_post", ctypes.c_void_p), ("norm_dt", ctypes.c_int), ("norm_eps", ctypes.c_double),
+                ("n_shared", ctypes.c_int), ("router_bias", ctypes.c_void_p)]
 
 
 def build(force: bool = True) -> str:
@@ -78,8 +79,8 @@ def _lib():
         lib.oracle_bf16_rne.restype = ctypes.c_uint16
         lib.oracle_capacity.argtypes = [ctypes.c_double, i64, ci, ci]
         lib.oracle_capacity.restype = i64
-        lib.oracle_route_v.argtypes = [vp, ci, vp, ci, i64, i64, ci, ci, ci, vp, vp, vp, ci]
-        lib.oracle_permute_cap.argtypes = [vp, i64, ci, ci, i64, vp, vp, vp, vp]
+        lib.oracle_route_v.argtypes = [vp, ci, vp, ci, i64, i64, ci, ci, ci, vp, vp, vp, vp, ci]
+        lib.oracle_permute_cap.argtypes = [vp, i64, ci, ci, i64, ci, vp, vp, vp, vp]
         lib.oracle_rmsnorm.argtypes = [vp, ci, i64, i64, vp, ci, ctypes.c_double, vp]
         lib.oracle_layer.argtypes = [ctypes.POINTER(_Layer), vp, i64, vp, vp, vp, vp, vp, ci]
         for name in ("oracle_route", "oracle_permute", "oracle_expert", "oracle_forward_given_routing",
@@ -248,33 +249,38 @@ def capacity(c: float, T: int, E: int, k: int) -> int:
     return int(_lib().oracle_capacity(float(c), T, E, k))
 
 
-def route_v(x: np.ndarray, router_w: np.ndarray, k: int, renormalize: bool = False, nthreads: int = 0):
-    """route() with the optional renormalisation of the k gates."""
+def route_v(x: np.ndarray, router_w: np.ndarray, k: int, renormalize: bool = False, bias=None,
+            nthreads: int = 0):
+    """route() with the optional selection bias (E fp32 values added to p for the top-k choice only)
+    and the optional renormalisation of the k gates."""
     x = np.ascontiguousarray(x)
     router_w = np.ascontiguousarray(router_w)
     T, d = x.shape
     E = router_w.shape[0]
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        assert bias.shape == (E,)
     probs = np.zeros((T, E), np.float64)
     idx = np.zeros((T, k), np.int32)
     gate = np.zeros((T, k), np.float64)
     rc = _lib().oracle_route_v(x.ctypes.data, _dt(x, True), router_w.ctypes.data, _dt(router_w, True), T, d, E, k,
-                               int(bool(renormalize)), probs.ctypes.data, idx.ctypes.data, gate.ctypes.data,
-                               nthreads or threads())
+                               int(bool(renormalize)), _c(bias), probs.ctypes.data, idx.ctypes.data,
+                               gate.ctypes.data, nthreads or threads())
     _check(rc, "route_v")
     return probs, idx, gate
 
 
-def permute_cap(idx: np.ndarray, E: int, cap: int):
-    """permute() with at most `cap` rows per expert (cap < 0: none). Dropped assignments get pos = -1;
-    perm holds offsets[E] valid rows (the rest of the array is zero)."""
+def permute_cap(idx: np.ndarray, E: int, cap: int, E_cap: Optional[int] = None):
+    """permute() with at most `cap` rows per expert e < E_cap (default all; cap < 0: none). Dropped
+    assignments get pos = -1; perm holds offsets[E] valid rows (the rest of the array is zero)."""
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     T, k = idx.shape
     counts = np.zeros(E, np.int32)
     offsets = np.zeros(E + 1, np.int32)
     perm = np.zeros(T * k, np.int32)
     pos = np.zeros((T, k), np.int32)
-    rc = _lib().oracle_permute_cap(idx.ctypes.data, T, E, k, int(cap), counts.ctypes.data, offsets.ctypes.data,
-                                   perm.ctypes.data, pos.ctypes.data)
+    rc = _lib().oracle_permute_cap(idx.ctypes.data, T, E, k, int(cap), E if E_cap is None else int(E_cap),
+                                   counts.ctypes.data, offsets.ctypes.data, perm.ctypes.data, pos.ctypes.data)
     _check(rc, "permute_cap")
     return counts, offsets, perm, pos
 
@@ -293,13 +299,22 @@ def rmsnorm(v: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
 
 def layer(x, router_w, w_gate, w_up, w_down, k: int, scales=None, activation: int = GELU,
           renormalize: bool = False, capacity_factor: float = 0.0, norm_pre=None, norm_post=None,
-          norm_eps: float = 1e-5, tokens: Optional[Sequence[int]] = None, nthreads: int = 0):
-    """The layer with its variants. Returns dict(out [ntok, d] f64, idx, gate, pos [T, k], u [T, d] or None)."""
+          norm_eps: float = 1e-5, n_shared: int = 0, router_bias=None, tokens: Optional[Sequence[int]] = None,
+          nthreads: int = 0):
+    """The layer with its variants. The weights hold E routed experts (router_w has E rows) followed by
+    n_shared shared experts. Returns dict(out [ntok, d] f64, idx, gate, pos [T, k + n_shared],
+    u [T, d] or None)."""
     x = np.ascontiguousarray(x)
     router_w = np.ascontiguousarray(router_w)
     w_gate, w_up, w_down, wdt, scales = _wargs(w_gate, w_up, w_down, scales)
-    E, f, d = w_gate.shape
+    Et, f, d = w_gate.shape
+    E = router_w.shape[0]
+    if Et != E + n_shared:
+        raise ValueError(f"weights hold {Et} experts, router {E} + {n_shared} shared")
     T = x.shape[0]
+    if router_bias is not None:
+        router_bias = np.ascontiguousarray(router_bias, dtype=np.float32)
+        assert router_bias.shape == (E,)
     L = _Layer()
     L.x, L.xdt = x.ctypes.data, _dt(x, True)
     L.router_w, L.rdt = router_w.ctypes.data, _dt(router_w, True)
@@ -315,12 +330,14 @@ def layer(x, router_w, w_gate, w_up, w_down, k: int, scales=None, activation: in
         L.norm_pre, L.norm_post, L.norm_dt = norm_pre.ctypes.data, norm_post.ctypes.data, _dt(norm_pre, True)
         u = np.zeros_like(x)
     L.norm_eps = float(norm_eps)
+    L.n_shared, L.router_bias = int(n_shared), _c(router_bias)
     tok = None if tokens is None else np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
     ntok = T if tok is None else tok.shape[0]
+    K = k + n_shared
     out = np.zeros((ntok, d), np.float64)
-    idx = np.zeros((T, k), np.int32)
-    gate = np.zeros((T, k), np.float64)
-    pos = np.zeros((T, k), np.int32)
+    idx = np.zeros((T, K), np.int32)
+    gate = np.zeros((T, K), np.float64)
+    pos = np.zeros((T, K), np.int32)
     rc = _lib().oracle_layer(ctypes.byref(L), _c(tok), ntok, out.ctypes.data, idx.ctypes.data, gate.ctypes.data,
                              pos.ctypes.data, _c(u), nthreads or threads())
     _check(rc, "layer")

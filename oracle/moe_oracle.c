@@ -48,6 +48,7 @@
 #endif
 
 enum { ORC_F64 = 0, ORC_F32 = 1, ORC_BF16 = 2, ORC_I8 = 3 };
+enum { ORC_MAXE = 512 }; /* experts a router may have */
 
 #define ORC_OK 0
 #define ORC_EINVAL (-1)
@@ -90,10 +91,13 @@ double oracle_gelu(double z) { return 0.5 * z * (1.0 + erf(z / sqrt(2.0))); }
 double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
 
 /* Steps 1-3 for one token: logits, softmax over all experts, top-k without
- * renormalisation (book ch. 10, section 10.3.1, the Grok-1 code). */
+ * renormalisation (book ch. 10, section 10.3.1, the Grok-1 code). With a
+ * selection bias b (nullable; the per-expert bias of DeepSeek-V3's
+ * aux-loss-free routing, book ch. 10, section 10.3.2), experts are chosen by
+ * p[e] + b[e] while the gates stay p[e]. */
 static void route_token(const void* x, int xdt, const void* wr, int rdt, int64_t t, int64_t d, int E,
-                        int k, double* p, int32_t* idx, double* gate) {
-  double logit[64];
+                        int k, const float* bias, double* p, int32_t* idx, double* gate) {
+  double logit[ORC_MAXE];
   for (int e = 0; e < E; ++e) {
     double s = 0.0;
     for (int64_t i = 0; i < d; ++i) s += elem(x, xdt, t * d + i) * elem(wr, rdt, (int64_t)e * d + i);
@@ -105,13 +109,15 @@ static void route_token(const void* x, int xdt, const void* wr, int rdt, int64_t
   double z = 0.0;
   for (int e = 0; e < E; ++e) z += exp(logit[e] - mx);
   for (int e = 0; e < E; ++e) p[e] = exp(logit[e] - mx) / z;
-  /* selection by the key (-p, e): largest probability first, lower index on ties */
-  int taken[64] = {0};
+  /* selection by the key (-(p + b), e): largest score first, lower index on ties */
+  double key[ORC_MAXE];
+  for (int e = 0; e < E; ++e) key[e] = bias ? p[e] + (double)bias[e] : p[e];
+  int taken[ORC_MAXE] = {0};
   for (int s = 0; s < k; ++s) {
     int best = -1;
     for (int e = 0; e < E; ++e) {
       if (taken[e]) continue;
-      if (best < 0 || p[e] > p[best]) best = e;
+      if (best < 0 || key[e] > key[best]) best = e;
     }
     taken[best] = 1;
     idx[s] = best;
@@ -122,14 +128,15 @@ static void route_token(const void* x, int xdt, const void* wr, int rdt, int64_t
 /* probs [T][E] (nullable), idx [T][k], gate [T][k]. */
 int oracle_route(const void* x, int xdt, const void* router_w, int rdt, int64_t T, int64_t d, int E, int k,
                  double* probs, int32_t* idx, double* gate, int nthreads) {
-  if (T < 0 || d < 1 || E < 1 || E > 64 || k < 1 || k > E || !valid_dt(xdt) || !valid_dt(rdt)) return ORC_EINVAL;
+  if (T < 0 || d < 1 || E < 1 || E > ORC_MAXE || k < 1 || k > E || !valid_dt(xdt) || !valid_dt(rdt))
+    return ORC_EINVAL;
   if (T > 0 && (!x || !router_w || !idx || !gate)) return ORC_EINVAL;
   int nt = set_threads(nthreads);
   (void)nt;
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
   for (int64_t t = 0; t < T; ++t) {
-    double p[64];
-    route_token(x, xdt, router_w, rdt, t, d, E, k, p, idx + t * k, gate + t * k);
+    double p[ORC_MAXE];
+    route_token(x, xdt, router_w, rdt, t, d, E, k, NULL, p, idx + t * k, gate + t * k);
     if (probs)
       for (int e = 0; e < E; ++e) probs[t * E + e] = p[e];
   }
@@ -293,7 +300,7 @@ int oracle_forward_given_routing(const void* x, int xdt, const void* wg, const v
 int oracle_forward(const void* x, int xdt, const void* router_w, int rdt, const void* wg, const void* wu,
                    const void* wd, int wdt, const float* scales, int64_t T, int64_t d, int64_t f, int E, int k,
                    double* out, int32_t* idx_out, double* gate_out, int nthreads) {
-  if (T < 0 || E < 1 || E > 64 || k < 1 || k > E) return ORC_EINVAL;
+  if (T < 0 || E < 1 || E > ORC_MAXE || k < 1 || k > E) return ORC_EINVAL;
   if (T == 0) return ORC_OK;
   int32_t* idx = idx_out ? idx_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * k));
   double* gate = gate_out ? gate_out : (double*)malloc(sizeof(double) * (size_t)(T * k));
@@ -318,7 +325,7 @@ int oracle_forward(const void* x, int xdt, const void* router_w, int rdt, const 
 int oracle_dense_onehot(const void* x, int xdt, const void* router_w, int rdt, const void* wg, const void* wu,
                         const void* wd, int wdt, const float* scales, int64_t T, int64_t d, int64_t f, int E,
                         int k, double* out, int nthreads) {
-  if (!check_weights(wdt, scales) || !valid_dt(xdt) || T < 0 || d < 1 || f < 1 || E < 1 || E > 64 || k < 1 ||
+  if (!check_weights(wdt, scales) || !valid_dt(xdt) || T < 0 || d < 1 || f < 1 || E < 1 || E > ORC_MAXE || k < 1 ||
       k > E)
     return ORC_EINVAL;
   weights_t w = {wg, wu, wd, wdt, scales, d, f, E, 0};
@@ -336,9 +343,9 @@ int oracle_dense_onehot(const void* x, int xdt, const void* router_w, int rdt, c
     } else {
 #pragma omp for schedule(dynamic, 1)
       for (int64_t t = 0; t < T; ++t) {
-        double p[64], g[64], mask[64];
-        int32_t id[64];
-        route_token(x, xdt, router_w, rdt, t, d, E, k, p, id, g);
+        double p[ORC_MAXE], g[ORC_MAXE], mask[ORC_MAXE];
+        int32_t id[ORC_MAXE];
+        route_token(x, xdt, router_w, rdt, t, d, E, k, NULL, p, id, g);
         for (int e = 0; e < E; ++e) mask[e] = 0.0;
         for (int s = 0; s < k; ++s) mask[id[s]] = g[s];
         for (int64_t i = 0; i < d; ++i) out[t * d + i] = 0.0;
@@ -391,7 +398,17 @@ int oracle_dense_onehot(const void* x, int xdt, const void* router_w, int rdt, c
  *    with RMSNorm(v; g)[i] = g[i] * v[i] / sqrt(mean_j v[j]^2 + eps). u is
  *    rounded to the activation type (bf16 or fp32, round to nearest even)
  *    because the router and the experts consume it as a stored tensor of a
- *    bf16 forward pass; MoE(u) and the post-norm stay in double. */
+ *    bf16 forward pass; MoE(u) and the post-norm stay in double.
+ *  - the fine-grained layout of DeepSeek-V3 (book ch. 10, section 10.1 table
+ *    and the shared-expert box; section 10.11.4): many small routed experts
+ *    plus n_shared shared experts that every token runs with gate 1, their
+ *    weights stored after the E routed experts' (E + n_shared experts in
+ *    w_gate/w_up/w_down and in the scales); and router_bias, a per-expert
+ *    bias of the aux-loss-free routing (section 10.3.2) that the pages say
+ *    shifts which experts are chosen: here it is added to the softmax
+ *    probabilities for the top-k choice only, the gates remain the
+ *    probabilities (then renormalised when asked). The capacity cap applies
+ *    to the routed experts only. */
 
 /* Round to the nearest bf16 value (8 significant bits), ties to even; returns
  * the bit pattern. Normal range only (|v| in [2^-126, 2^128)) and zero. */
@@ -412,12 +429,24 @@ int64_t oracle_capacity(double c, int64_t T, int E, int k) {
   return (int64_t)floor(c * (double)(k * T) / (double)E);
 }
 
-/* Routing with the optional renormalisation: gates divided by their sum over
- * the k slots (summed in slot order). */
+/* Routing with the optional selection bias (nullable, E values) and the
+ * optional renormalisation: gates divided by their sum over the k slots
+ * (summed in slot order). */
 int oracle_route_v(const void* x, int xdt, const void* router_w, int rdt, int64_t T, int64_t d, int E, int k,
-                   int renormalize, double* probs, int32_t* idx, double* gate, int nthreads) {
-  int rc = oracle_route(x, xdt, router_w, rdt, T, d, E, k, probs, idx, gate, nthreads);
-  if (rc != ORC_OK || !renormalize) return rc;
+                   int renormalize, const float* bias, double* probs, int32_t* idx, double* gate, int nthreads) {
+  if (T < 0 || d < 1 || E < 1 || E > ORC_MAXE || k < 1 || k > E || !valid_dt(xdt) || !valid_dt(rdt))
+    return ORC_EINVAL;
+  if (T > 0 && (!x || !router_w || !idx || !gate)) return ORC_EINVAL;
+  int nt = set_threads(nthreads);
+  (void)nt;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+  for (int64_t t = 0; t < T; ++t) {
+    double p[ORC_MAXE];
+    route_token(x, xdt, router_w, rdt, t, d, E, k, bias, p, idx + t * k, gate + t * k);
+    if (probs)
+      for (int e = 0; e < E; ++e) probs[t * E + e] = p[e];
+  }
+  if (!renormalize) return ORC_OK;
   for (int64_t t = 0; t < T; ++t) {
     double sum = 0.0;
     for (int s = 0; s < k; ++s) sum += gate[t * k + s];
@@ -426,11 +455,13 @@ int oracle_route_v(const void* x, int xdt, const void* router_w, int rdt, int64_
   return ORC_OK;
 }
 
-/* Permutation with a per-expert cap (cap < 0: none). For every expert, its
- * assignments are ranked by token index; those of rank >= cap are dropped
- * (pos = -1, no row). counts are the kept assignments, offsets their
- * exclusive scan, and segment e lists its kept tokens in ascending order. */
-int oracle_permute_cap(const int32_t* idx, int64_t T, int E, int k, int64_t cap, int32_t* counts,
+/* Permutation with a per-expert cap (cap < 0: none) on the experts e <
+ * E_cap (the routed ones; shared experts are never capped). For every capped
+ * expert, its assignments are ranked by token index; those of rank >= cap
+ * are dropped (pos = -1, no row). counts are the kept assignments, offsets
+ * their exclusive scan, and segment e lists its kept tokens in ascending
+ * order. */
+int oracle_permute_cap(const int32_t* idx, int64_t T, int E, int k, int64_t cap, int E_cap, int32_t* counts,
                        int32_t* offsets, int32_t* perm, int32_t* pos) {
   if (T < 0 || E < 1 || k < 1 || k > E || !counts || !offsets) return ORC_EINVAL;
   int64_t* seen = (int64_t*)calloc((size_t)E, sizeof(int64_t));
@@ -441,7 +472,7 @@ int oracle_permute_cap(const int32_t* idx, int64_t T, int E, int k, int64_t cap,
     if (e < 0 || e >= E) { free(seen); return ORC_EINVAL; }
     seen[e] += 1;
   }
-  for (int e = 0; e < E; ++e) counts[e] = (int32_t)((cap >= 0 && seen[e] > cap) ? cap : seen[e]);
+  for (int e = 0; e < E; ++e) counts[e] = (int32_t)((cap >= 0 && e < E_cap && seen[e] > cap) ? cap : seen[e]);
   offsets[0] = 0;
   for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
   /* pass 2: walk the tokens in order; an expert's rank-th assignment gets row
@@ -490,7 +521,7 @@ typedef struct {
   int wdt;
   const float* scales;
   int64_t T, d, f;
-  int E, k;
+  int E, k; /* routed experts and how many each token picks */
   int act;
   int renormalize;
   double capacity_factor;
@@ -498,15 +529,19 @@ typedef struct {
   const void* norm_post;
   int norm_dt;
   double norm_eps;
+  int n_shared;            /* experts E .. E + n_shared - 1 of the weights run on every token, gate 1 */
+  const float* router_bias; /* nullable, E values: added to p for the top-k choice only */
 } orc_layer;
 
 /* The layer with its variants: routing and permutation for all T tokens, then
  * the outputs of the listed tokens (all T when tokens is NULL; ntok rows of d
- * values in out). Optional outputs: idx/gate [T][k], pos [T][k] (-1 =
- * dropped), u (T*d values of type xdt, the stored pre-norm output). */
+ * values in out). Optional outputs: idx/gate/pos [T][K] with K = k + n_shared
+ * (slots k.. are the shared experts; pos -1 = dropped), u (T*d values of type
+ * xdt, the stored pre-norm output). */
 int oracle_layer(const orc_layer* L, const int64_t* tokens, int64_t ntok, double* out, int32_t* idx_out,
                  double* gate_out, int32_t* pos_out, void* u_out, int nthreads) {
-  if (!L || L->T < 0 || L->d < 1 || L->f < 1 || L->E < 1 || L->E > 64 || L->k < 1 || L->k > L->E) return ORC_EINVAL;
+  if (!L || L->T < 0 || L->d < 1 || L->f < 1 || L->E < 1 || L->E > ORC_MAXE || L->k < 1 || L->k > L->E) return ORC_EINVAL;
+  if (L->n_shared < 0 || L->n_shared > 64) return ORC_EINVAL;
   if (L->xdt != ORC_BF16 && L->xdt != ORC_F32) return ORC_EINVAL;
   if (!check_weights(L->wdt, L->scales) || (L->act != 0 && L->act != 1)) return ORC_EINVAL;
   if ((L->norm_pre == NULL) != (L->norm_post == NULL)) return ORC_EINVAL;
@@ -514,7 +549,8 @@ int oracle_layer(const orc_layer* L, const int64_t* tokens, int64_t ntok, double
   if (sandwich && (!valid_dt(L->norm_dt) || !(L->norm_eps >= 0.0))) return ORC_EINVAL;
   if (!tokens && ntok != L->T) return ORC_EINVAL;
   const int64_t T = L->T, d = L->d, f = L->f;
-  const int E = L->E, k = L->k;
+  const int E = L->E, kr = L->k;            /* routed experts, routed slots */
+  const int Et = E + L->n_shared, k = kr + L->n_shared; /* all experts, all slots */
   if (T == 0) return ORC_OK;
   for (int64_t r = 0; r < ntok; ++r)
     if (tokens && (tokens[r] < 0 || tokens[r] >= T)) return ORC_EINVAL;
@@ -526,10 +562,13 @@ int oracle_layer(const orc_layer* L, const int64_t* tokens, int64_t ntok, double
   double* gate = (double*)malloc(sizeof(double) * (size_t)(T * k));
   int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * k));
   int32_t* perm = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * k));
-  int32_t counts[64], offsets[65];
+  int32_t* counts = (int32_t*)malloc(sizeof(int32_t) * (size_t)Et);
+  int32_t* offsets = (int32_t*)malloc(sizeof(int32_t) * (size_t)(Et + 1));
+  int32_t* ridx = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * kr));
+  double* rgate = (double*)malloc(sizeof(double) * (size_t)(T * kr));
   double* y = (double*)malloc(sizeof(double) * (size_t)(ntok * k * d + 1));
   int rc = ORC_ENOMEM;
-  if (!idx || !gate || !pos || !perm || !y) goto done;
+  if (!idx || !gate || !pos || !perm || !y || !counts || !offsets || !ridx || !rgate) goto done;
 
   /* 1. the MoE input: x, or the pre-norm of x stored in the activation type */
   const void* a = L->x;
@@ -548,15 +587,29 @@ int oracle_layer(const orc_layer* L, const int64_t* tokens, int64_t ntok, double
     }
     a = u;
   }
-  /* 2. routing (softmax, top-k, optional renormalisation) */
-  rc = oracle_route_v(a, L->xdt, L->router_w, L->rdt, T, d, E, k, L->renormalize, NULL, idx, gate, nthreads);
+  /* 2. routing over the routed experts (softmax, top-k by p + bias, optional
+   *    renormalisation), then the shared experts' slots with gate 1 */
+  rc = oracle_route_v(a, L->xdt, L->router_w, L->rdt, T, d, E, kr, L->renormalize, L->router_bias, NULL, ridx,
+                      rgate, nthreads);
   if (rc != ORC_OK) goto done;
-  /* 3. permutation with the capacity cap: decides which assignments run */
-  rc = oracle_permute_cap(idx, T, E, k, oracle_capacity(L->capacity_factor, T, E, k), counts, offsets, perm, pos);
+  for (int64_t t = 0; t < T; ++t) {
+    for (int s = 0; s < kr; ++s) {
+      idx[t * k + s] = ridx[t * kr + s];
+      gate[t * k + s] = rgate[t * kr + s];
+    }
+    for (int j = 0; j < L->n_shared; ++j) {
+      idx[t * k + kr + j] = E + j;
+      gate[t * k + kr + j] = 1.0;
+    }
+  }
+  /* 3. permutation with the capacity cap on the routed experts: decides which
+   *    assignments run */
+  rc = oracle_permute_cap(idx, T, Et, k, oracle_capacity(L->capacity_factor, T, E, kr), E, counts, offsets, perm,
+                          pos);
   if (rc != ORC_OK) goto done;
   /* 4. expert outputs of the kept assignments of the listed tokens */
   {
-    weights_t w = {L->wg, L->wu, L->wd, L->wdt, L->scales, d, f, E, L->act};
+    weights_t w = {L->wg, L->wu, L->wd, L->wdt, L->scales, d, f, Et, L->act};
     int nt = set_threads(nthreads);
     (void)nt;
     int fail = 0;
@@ -615,5 +668,9 @@ done:
   free(y);
   free(u);
   free(tmp);
+  free(counts);
+  free(offsets);
+  free(ridx);
+  free(rgate);
   return rc;
 }

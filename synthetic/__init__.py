@@ -23,12 +23,15 @@ Storage layouts (all row-major, contiguous):
 
 Tensor ids for the counter-based generator: x=0, router=1, gate=2, up=3,
 down=4, pre-norm weights=5, post-norm weights=6 (7: the test-only random
-scales).
+scales), router selection bias=8.
 
 Variants beside the Grok-1 layer: the Mixtral 8x22B shape (d = 6144,
 f = 16384, 8 experts, top-2; book ch. 10, section 10.1 table) with SiLU
 experts and renormalised gates; the sandwich sub-layer (RMSNorm weights
-before and after the MoE); a capacity factor.
+before and after the MoE); a capacity factor; the fine-grained DeepSeek-V3
+layout (d = 7168, 256 routed experts of width 2048, top-8, one shared expert,
+a per-expert selection bias; book ch. 10, section 10.1 table and sections
+10.3.2 and 10.11.4), whose shared expert's weights follow the routed ones.
 """
 from __future__ import annotations
 
@@ -47,6 +50,8 @@ _LIB = os.path.join(_HERE, "libsynthetic.so")
 _lib_handle = None
 
 TID_X, TID_ROUTER, TID_GATE, TID_UP, TID_DOWN, TID_NORM_PRE, TID_NORM_POST = 0, 1, 2, 3, 4, 5, 6
+TID_ROUTER_BIAS = 8
+ROUTER_BIAS_STD = 1e-3   # selection bias scale, against probabilities of about 1/256
 
 
 def build(force: bool = True) -> str:
@@ -151,6 +156,8 @@ class Workload:
     norm_pre: Optional[np.ndarray] = None   # [d], activation dtype (sandwich sub-layer)
     norm_post: Optional[np.ndarray] = None
     norm_eps: float = 1e-5
+    n_shared: int = 0                   # shared experts stored after the E routed ones
+    router_bias: Optional[np.ndarray] = None  # [E] fp32 selection bias
 
     @property
     def weight_bytes(self) -> int:
@@ -172,12 +179,17 @@ WORKLOADS = {
     # Mixtral 8x22B-shape decode step and full-context prefill (SiLU, renormalised gates).
     "mixtral_decode": (8, 6144, 16384, 8, 2, "bf16", "bf16", False),
     "mixtral_prefill": (8192, 6144, 16384, 8, 2, "bf16", "bf16", False),
+    # DeepSeek-V3-shape fine-grained layer: 256 routed experts of width 2048, top-8, plus one shared expert.
+    "dsv3_decode": (8, 7168, 2048, 256, 8, "bf16", "bf16", False),
+    "dsv3_prefill": (8192, 7168, 2048, 256, 8, "bf16", "bf16", False),
 }
 
 # name -> variant knobs that differ from the Grok-1 layer
 VARIANTS = {
     "mixtral_decode": dict(activation="silu", renormalize=True),
     "mixtral_prefill": dict(activation="silu", renormalize=True),
+    "dsv3_decode": dict(activation="silu", renormalize=True, n_shared=1, router_bias=True),
+    "dsv3_prefill": dict(activation="silu", renormalize=True, n_shared=1, router_bias=True),
 }
 
 
@@ -200,11 +212,13 @@ def make(name: str = "decode", seed: int = 0, T: Optional[int] = None, d: Option
          act_dtype: Optional[str] = None, w_dtype: Optional[str] = None,
          skew: Optional[bool] = None, with_weights: bool = True, activation: Optional[str] = None,
          renormalize: Optional[bool] = None, capacity_factor: Optional[float] = None,
-         sandwich: bool = False, norm_eps: float = 1e-5) -> Workload:
+         sandwich: bool = False, norm_eps: float = 1e-5, n_shared: Optional[int] = None,
+         router_bias: Optional[bool] = None) -> Workload:
     """Build a named workload; any size, dtype or variant knob can be overridden (for small parity cases).
 
     with_weights=False leaves the expert weights as empty placeholders (routing-only checks).
-    sandwich=True adds the RMSNorm weights of the sandwich sub-layer.
+    sandwich=True adds the RMSNorm weights of the sandwich sub-layer; n_shared appends that many shared
+    experts to the weights; router_bias=True draws a per-expert selection bias.
     """
     T0, d0, f0, E0, k0, a0, w0, s0 = WORKLOADS[name]
     T = T0 if T is None else T
@@ -215,6 +229,13 @@ def make(name: str = "decode", seed: int = 0, T: Optional[int] = None, d: Option
     act = a0 if act_dtype is None else act_dtype
     wdt = w0 if w_dtype is None else w_dtype
     skew = s0 if skew is None else skew
+    var = dict(activation="gelu", renormalize=False, capacity_factor=0.0, n_shared=0, router_bias=False)
+    var.update(VARIANTS.get(name, {}))
+    for key, val in (("activation", activation), ("renormalize", renormalize), ("capacity_factor", capacity_factor),
+                     ("n_shared", n_shared), ("router_bias", router_bias)):
+        if val is not None:
+            var[key] = val
+    Et = E + var["n_shared"]   # experts in the weight tensors
 
     x = normal((T, d), seed, TID_X, 1.0, act)
     rdt = "f32" if act == "f32" else "bf16"
@@ -223,17 +244,17 @@ def make(name: str = "decode", seed: int = 0, T: Optional[int] = None, d: Option
     if not with_weights:
         w_gate = w_up = w_down = np.zeros((0,), np.uint16)
     elif wdt == "i8":
-        w_gate = uniform_i8((E, f, d), seed, TID_GATE)
-        w_up = uniform_i8((E, f, d), seed, TID_UP)
-        w_down = uniform_i8((E, d, f), seed, TID_DOWN)
+        w_gate = uniform_i8((Et, f, d), seed, TID_GATE)
+        w_up = uniform_i8((Et, f, d), seed, TID_UP)
+        w_down = uniform_i8((Et, d, f), seed, TID_DOWN)
         s_in = np.float32(1.0 / (127.0 * math.sqrt(d)))
         s_ff = np.float32(1.0 / (127.0 * math.sqrt(f)))
-        scales = np.concatenate([np.full(E * f, s_in, np.float32), np.full(E * f, s_in, np.float32),
-                                 np.full(E * d, s_ff, np.float32)])
+        scales = np.concatenate([np.full(Et * f, s_in, np.float32), np.full(Et * f, s_in, np.float32),
+                                 np.full(Et * d, s_ff, np.float32)])
     else:
-        w_gate = normal((E, f, d), seed, TID_GATE, 1.0 / math.sqrt(d), wdt)
-        w_up = normal((E, f, d), seed, TID_UP, 1.0 / math.sqrt(d), wdt)
-        w_down = normal((E, d, f), seed, TID_DOWN, 1.0 / math.sqrt(f), wdt)
+        w_gate = normal((Et, f, d), seed, TID_GATE, 1.0 / math.sqrt(d), wdt)
+        w_up = normal((Et, f, d), seed, TID_UP, 1.0 / math.sqrt(d), wdt)
+        w_down = normal((Et, d, f), seed, TID_DOWN, 1.0 / math.sqrt(f), wdt)
     notes = {}
     if skew:
         one = np.float32(1.0)
@@ -249,19 +270,13 @@ def make(name: str = "decode", seed: int = 0, T: Optional[int] = None, d: Option
         else:
             router_w[:, d - 1] = f32_to_bf16_bits(bias)
         notes["skew"] = "x[:, d-1] = 1.0; router_w[:, d-1] = (+3.0, +1.5, 0, ...)"
-    var = dict(activation="gelu", renormalize=False, capacity_factor=0.0)
-    var.update(VARIANTS.get(name, {}))
-    if activation is not None:
-        var["activation"] = activation
-    if renormalize is not None:
-        var["renormalize"] = renormalize
-    if capacity_factor is not None:
-        var["capacity_factor"] = capacity_factor
     if var["activation"] not in ("gelu", "silu"):
         raise ValueError(f"unknown activation {var['activation']}")
     norm_pre = norm_post = None
     if sandwich:
         norm_pre, norm_post = norm_weights(d, seed, act)
+    var["router_bias"] = (normal((E,), seed, TID_ROUTER_BIAS, ROUTER_BIAS_STD, "f32")
+                          if var["router_bias"] else None)
     return Workload(name=name, T=T, d=d, f=f, E=E, k=k, act_dtype=act, w_dtype=wdt, x=x,
                     router_w=router_w, w_gate=w_gate, w_up=w_up, w_down=w_down, scales=scales,
                     seed=seed, notes=notes, norm_pre=norm_pre, norm_post=norm_post, norm_eps=norm_eps, **var)

@@ -1,6 +1,7 @@
 """Pins for the oracle's layer variants: SiLU experts, renormalised gates,
-capacity-factor drops and the sandwich sub-layer (RMSNorm before and after the
-MoE, plus the residual).
+capacity-factor drops, the sandwich sub-layer (RMSNorm before and after the
+MoE, plus the residual), and the fine-grained layout (hundreds of experts, a
+per-expert selection bias, shared experts).
 
 As in test_oracle_pins.py, every check compares the oracle with something
 other than itself: closed forms, brute force written here with numpy/scipy
@@ -189,12 +190,14 @@ def test_rmsnorm_invariants():
 
 # ---------------------------------------------------------------- whole layer with variants
 def _brute_dense_layer(w, act, renorm, cap, tokens=None):
-    """Every expert on every token with numpy products, then one-hot(kept top-k) * gate."""
+    """Every expert on every token with numpy products, then one-hot(kept top-k) * gate, plus the
+    shared experts (after the routed ones in the weights) with gate 1."""
     x = _f64(w.x)
     wr = _f64(w.router_w)
     logits = x @ wr.T
     p = scipy.special.softmax(logits, axis=1)
-    order = np.lexsort((np.arange(w.E)[None, :].repeat(w.T, 0), -p), axis=1)  # key (-p, e)
+    key = p if w.router_bias is None else p + w.router_bias.astype(np.float64)[None, :]
+    order = np.lexsort((np.arange(w.E)[None, :].repeat(w.T, 0), -key), axis=1)  # key (-(p + b), e)
     idx = order[:, :w.k]
     gate = np.take_along_axis(p, idx, axis=1)
     if renorm:
@@ -215,6 +218,11 @@ def _brute_dense_layer(w, act, renorm, cap, tokens=None):
         y = (fn(a) * b) @ _f64(w.w_down[e]).T
         m = np.where((idx == e) & keep, gate, 0.0).sum(axis=1)
         out += m[:, None] * y
+    for j in range(w.n_shared):
+        e = w.E + j
+        a = x @ _f64(w.w_gate[e]).T
+        b = x @ _f64(w.w_up[e]).T
+        out += (fn(a) * b) @ _f64(w.w_down[e]).T
     return out, idx, gate, keep
 
 
@@ -222,7 +230,8 @@ def _layer(w, **kw):
     return oracle.layer(w.x, w.router_w, w.w_gate, w.w_up, w.w_down, w.k, scales=w.scales,
                         activation=oracle.SILU if w.activation == "silu" else oracle.GELU,
                         renormalize=w.renormalize, capacity_factor=w.capacity_factor,
-                        norm_pre=w.norm_pre, norm_post=w.norm_post, norm_eps=w.norm_eps, **kw)
+                        norm_pre=w.norm_pre, norm_post=w.norm_post, norm_eps=w.norm_eps, n_shared=w.n_shared,
+                        router_bias=w.router_bias, **kw)
 
 
 def test_layer_with_variants_off_equals_forward():
@@ -242,9 +251,9 @@ def test_layer_variants_match_dense_brute_force(act, renorm, cf):
     r = _layer(w)
     cap = oracle.capacity(cf, w.T, w.E, w.k)
     ref, idx, gate, keep = _brute_dense_layer(w, act, renorm, cap)
-    np.testing.assert_array_equal(r["idx"], idx)
-    np.testing.assert_allclose(r["gate"], gate, rtol=1e-12)
-    np.testing.assert_array_equal(r["pos"] >= 0, keep)
+    np.testing.assert_array_equal(r["idx"][:, :w.k], idx)
+    np.testing.assert_allclose(r["gate"][:, :w.k], gate, rtol=1e-12)
+    np.testing.assert_array_equal(r["pos"][:, :w.k] >= 0, keep)
     np.testing.assert_allclose(r["out"], ref, rtol=1e-10, atol=1e-12)
     if cf > 0:
         assert (~keep).any(), "the skewed workload must overflow at this capacity"
@@ -351,3 +360,80 @@ def test_layer_rejects_bad_arguments():
     with pytest.raises(RuntimeError):
         oracle.layer(w.x, w.router_w, w.w_gate, w.w_up, w.w_down, 2, norm_pre=np.ones(64, np.float32),
                      norm_post=np.ones(64, np.float32), norm_eps=-1.0)
+
+
+# ---------------------------------------------------------------- fine-grained: many experts, bias, shared experts
+def test_selection_bias_on_equal_probabilities():
+    # zero router: every p = 1/E, so the bias alone decides the choice (ties to the lower index),
+    # and the gates stay the probabilities: 1/E each, 1/k after renormalisation
+    E, k = 32, 4
+    x = synthetic.normal((6, 64), 0, 0, 1.0, "bf16")
+    wr = np.zeros((E, 64), np.uint16)
+    b = np.zeros(E, np.float32)
+    b[[5, 17, 30]] = [0.3, 0.2, 0.1]
+    b[[9, 2]] = 0.05
+    _, idx, gate = oracle.route_v(x, wr, k, renormalize=False, bias=b)
+    assert (idx == [5, 17, 30, 2]).all()                 # 2 before 9 at equal bias
+    np.testing.assert_allclose(gate, 1.0 / E, rtol=1e-15)
+    _, idx, gate = oracle.route_v(x, wr, k, renormalize=True, bias=b)
+    np.testing.assert_allclose(gate, 1.0 / k, rtol=1e-15)
+
+
+def test_selection_bias_forces_an_expert_but_not_its_gate():
+    w = synthetic.make("decode", T=40, d=256, E=16, k=2, with_weights=False)
+    b = np.zeros(16, np.float32)
+    b[11] = 10.0
+    probs, idx, gate = oracle.route_v(w.x, w.router_w, 2, bias=b)
+    assert (idx[:, 0] == 11).all()
+    np.testing.assert_array_equal(gate[:, 0], probs[:, 11])   # the gate is the unbiased probability
+    _, idx0, _ = oracle.route_v(w.x, w.router_w, 2)
+    np.testing.assert_array_equal(idx[:, 1], np.where(idx0[:, 0] == 11, idx0[:, 1], idx0[:, 0]))
+
+
+@pytest.mark.parametrize("E,k,bias", [(256, 8, True), (256, 8, False), (160, 6, True), (512, 3, False)])
+def test_many_expert_routing_brute_force(E, k, bias):
+    w = synthetic.make("dsv3_decode", T=48, d=256, E=E, k=k, with_weights=False, router_bias=bias)
+    probs, idx, gate = oracle.route_v(w.x, w.router_w, k, renormalize=True, bias=w.router_bias)
+    p = scipy.special.softmax(_f64(w.x) @ _f64(w.router_w).T, axis=1)
+    np.testing.assert_allclose(probs, p, rtol=1e-12, atol=1e-18)
+    key = p if w.router_bias is None else p + w.router_bias.astype(np.float64)
+    order = np.lexsort((np.arange(E)[None, :].repeat(w.T, 0), -key), axis=1)[:, :k]
+    np.testing.assert_array_equal(idx, order)
+    sel = np.take_along_axis(p, order, axis=1)
+    np.testing.assert_allclose(gate, sel / sel.sum(axis=1, keepdims=True), rtol=1e-12)
+
+
+def test_capacity_spares_shared_experts():
+    idx = np.array([[0, 4], [0, 4], [0, 4], [1, 4]], np.int32)   # expert 4 is the shared one (E_cap = 4)
+    c, o, p, pos = oracle.permute_cap(idx, 5, 1, E_cap=4)
+    assert list(c) == [1, 1, 0, 0, 4]
+    assert (pos[:, 1] >= 0).all() and list(pos[:, 0]) == [0, -1, -1, 1]
+
+
+@pytest.mark.parametrize("act,renorm,cf,bias", [("silu", True, 0.0, True), ("gelu", False, 0.0, False),
+                                                ("silu", True, 0.6, True)])
+def test_shared_expert_layer_matches_dense_brute_force(act, renorm, cf, bias):
+    w = synthetic.make("dsv3_decode", T=24, d=64, f=96, E=16, k=4, activation=act, renormalize=renorm,
+                       capacity_factor=cf, router_bias=bias, act_dtype="f32", w_dtype="f32")
+    assert w.n_shared == 1 and w.w_gate.shape[0] == 17
+    r = _layer(w)
+    assert r["idx"].shape == (24, 5)
+    assert (r["idx"][:, 4] == 16).all() and (r["gate"][:, 4] == 1.0).all() and (r["pos"][:, 4] >= 0).all()
+    cap = oracle.capacity(cf, w.T, w.E, w.k)
+    ref, idx, gate, keep = _brute_dense_layer(w, act, renorm, cap)
+    np.testing.assert_array_equal(r["idx"][:, :4], idx)
+    np.testing.assert_allclose(r["gate"][:, :4], gate, rtol=1e-12)
+    np.testing.assert_array_equal(r["pos"][:, :4] >= 0, keep)
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_shared_expert_alone_is_a_dense_ffn():
+    # routed experts' down projections zero: the layer is the shared expert's SwiGLU FFN on every token
+    w = synthetic.make("dsv3_decode", T=10, d=128, f=64, E=8, k=2)
+    w.w_down = w.w_down.copy()
+    w.w_down[:8] = 0
+    r = _layer(w)
+    x = _f64(w.x)
+    a = x @ _f64(w.w_gate[8]).T
+    y = (a * scipy.special.expit(a) * (x @ _f64(w.w_up[8]).T)) @ _f64(w.w_down[8]).T
+    np.testing.assert_allclose(r["out"], y, rtol=1e-12, atol=1e-14)
