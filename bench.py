@@ -12,7 +12,9 @@ the dominant kernel measured live with HIP events on the launch stream, and
 the CPU oracle timed on the host as a reported baseline.
 
 Variants (not the headline): --workload mixtral_decode / mixtral_prefill (Mixtral
-8x22B expert shapes, SiLU experts, renormalised gates), --sandwich (RMSNorm
+8x22B expert shapes, SiLU experts, renormalised gates), dsv3_decode /
+dsv3_prefill (DeepSeek-V3-shape fine-grained layer: 256 routed experts of
+width 2048, top-8, one shared expert, a selection bias), --sandwich (RMSNorm
 before and after the MoE plus the residual), --capacity c (capacity factor).
 """
 from __future__ import annotations
@@ -41,6 +43,8 @@ WORKLOAD_NAMES = {
     "tiny_f32": "tiny_moe_layer_f32_T64",
     "mixtral_decode": "mixtral8x22b_moe_layer_decode_T8",
     "mixtral_prefill": "mixtral8x22b_moe_layer_prefill_T8192",
+    "dsv3_decode": "dsv3_moe_layer_decode_T8",
+    "dsv3_prefill": "dsv3_moe_layer_prefill_T8192",
 }
 
 
@@ -132,14 +136,16 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(a).cuda()
 
-    x, rw, wg, wu, wd, sc, npre, npost = (dev(getattr(w, n)) for n in ("x", "router_w", "w_gate", "w_up", "w_down",
-                                                                       "scales", "norm_pre", "norm_post"))
+    x, rw, wg, wu, wd, sc, npre, npost, rbias = (
+        dev(getattr(w, n)) for n in ("x", "router_w", "w_gate", "w_up", "w_down", "scales", "norm_pre", "norm_post",
+                                     "router_bias"))
     variant = dict(activation=gm.ACT_SILU if w.activation == "silu" else gm.ACT_GELU, renormalize=w.renormalize,
-                   capacity_factor=w.capacity_factor, norm_pre=npre, norm_post=npost, norm_eps=w.norm_eps)
+                   capacity_factor=w.capacity_factor, norm_pre=npre, norm_post=npost, norm_eps=w.norm_eps,
+                   n_shared=w.n_shared, router_bias=rbias)
     torch.cuda.synchronize()
     log("inputs resident in HBM")
     out = torch.empty_like(x)
-    need = gm.grok_moe_workspace_bytes(w.T, w.d, w.f, w.E, w.k, gm._dtype_code(x), gm._dtype_code(wg))
+    need = gm.grok_moe_workspace_bytes_ex(x, rw, wg, wu, wd, k=w.k, **variant)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
@@ -147,6 +153,8 @@ def main():
     _, dbg = gm.grok_moe_forward_ex(x, rw, wg, wu, wd, k=w.k, scales=sc, out=out, workspace=ws, debug=True, **variant)
     torch.cuda.synchronize()
     counts = dbg["counts"].cpu().numpy()
+    if args.shard == "ep8" and w.n_shared:
+        raise SystemExit("--shard ep8 models layers without shared experts")
     if args.shard == "ep8":
         # one expert per GPU: the busiest expert's GPU runs that expert on its routed rows
         # (gate 1 with E = 1, k = 1); the all-to-all that brings the rows is not modelled
@@ -162,10 +170,10 @@ def main():
             sc = torch.from_numpy(sc_e).cuda()
         w = dataclasses.replace(w, T=len(tok), E=1, k=1, x=w.x[tok], router_w=w.router_w[e:e + 1],
                                 w_gate=w.w_gate[e:e + 1], w_up=w.w_up[e:e + 1], w_down=w.w_down[e:e + 1],
-                                scales=sc_e, renormalize=False, capacity_factor=0.0)
+                                scales=sc_e, renormalize=False, capacity_factor=0.0, router_bias=None)
         ti = torch.from_numpy(tok).cuda()
         x, rw, wg, wu, wd = x[ti].contiguous(), rw[e:e + 1], wg[e:e + 1], wu[e:e + 1], wd[e:e + 1]
-        variant.update(renormalize=False, capacity_factor=0.0)
+        variant.update(renormalize=False, capacity_factor=0.0, router_bias=None)
         workload += f"_ep8_expert{e}_M{w.T}"
         log(f"expert-parallel share: expert {e}, {w.T} rows")
         out = torch.empty_like(x)
@@ -214,6 +222,7 @@ def main():
         gu_bytes += n_hit * 2 * w.f * 4
     gu_flops = 4.0 * rows * w.d * w.f
     layer_bytes = (n_hit * 3 * w.d * w.f * wbytes + 2 * w.T * w.d * abytes + w.E * w.d * abytes)
+    # rows counts every (token, expert) pair that runs, shared experts included
     layer_flops = 6.0 * rows * w.d * w.f + 2.0 * w.T * w.d * w.E
     gu_s = stage_ms["gate_up"] / 1e3
     hbm_bound = gu_flops / gu_bytes < (MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS) * 1e3
@@ -250,7 +259,7 @@ def main():
         "config": {"workload": workload, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k,
                    "weights": w.w_dtype, "experts_hit": n_hit, "activation": w.activation,
                    "renormalize": w.renormalize, "capacity_factor": w.capacity_factor, "sandwich": args.sandwich,
-                   "rows_run": rows},
+                   "n_shared": w.n_shared, "router_bias": w.router_bias is not None, "rows_run": rows},
         "roofline": roof,
         "cpu_baseline": cpu,
         "layer": {"ms": round(ms_per_step, 5), "GBps": round(layer_bytes / (ms_per_step / 1e3) / 1e9, 1),
@@ -275,7 +284,7 @@ def cpu_baseline(w, name, args):
         oracle.layer(w.x[:n], w.router_w, w.w_gate, w.w_up, w.w_down, w.k, scales=w.scales,
                      activation=oracle.SILU if w.activation == "silu" else oracle.GELU, renormalize=w.renormalize,
                      capacity_factor=w.capacity_factor, norm_pre=w.norm_pre, norm_post=w.norm_post,
-                     norm_eps=w.norm_eps, nthreads=cores)
+                     norm_eps=w.norm_eps, n_shared=w.n_shared, router_bias=w.router_bias, nthreads=cores)
         passes += 1
         dt = time.perf_counter() - t0
     return {"value": round(n * passes / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",

@@ -40,8 +40,9 @@
  *    enqueues nothing and writes nothing.
  *  - `out` must not alias any input. T = 0 is a no-op that returns OK.
  *  - Supported shapes (GROK_MOE_EUNSUPPORTED otherwise): 1 <= k <= min(E, 8),
- *    E <= 64, bf16 and 8-bit weights need d % 256 == 0 and f % 256 == 0;
- *    fp32 needs d % 8 == 0 and f % 4 == 0; T <= 2^20.
+ *    E <= 256 routed experts (E <= 64 with fp32 activations), at most 4
+ *    shared experts; bf16 and 8-bit weights need d % 256 == 0 and
+ *    f % 256 == 0; fp32 needs d % 8 == 0 and f % 4 == 0; T <= 2^20.
  *  - Pointers must be 16-byte aligned (GROK_MOE_EALIGN otherwise).
  *  - Thread-safe: no global mutable state. Concurrent calls on different
  *    streams need separate workspaces (the plain forms allocate their own).
@@ -103,7 +104,19 @@ enum { GROK_MOE_ACT_GELU = 0, GROK_MOE_ACT_SILU = 1 };
  *                   the router and the experts see u. Dropped assignments
  *                   leave a token's MoE sum at zero, so out = x for a token
  *                   whose every assignment overflowed.
- *  norm_eps         eps of both norms (>= 0, finite). */
+ *  norm_eps         eps of both norms (>= 0, finite).
+ *  n_shared         shared experts (0..4; DeepSeek-style fine-grained layers,
+ *                   book ch. 10, section 10.1 table and the shared-expert
+ *                   box): w_gate, w_up, w_down and scales then hold
+ *                   E + n_shared experts, the shared ones last, and every
+ *                   token also runs each of them with gate 1 (after the
+ *                   routed gates, never capped). The debug idx/gate/pos
+ *                   arrays then have k + n_shared columns, the shared slots
+ *                   last; counts/offsets cover E + n_shared experts.
+ *  router_bias      NULL, or E fp32 values: a per-expert bias of the
+ *                   aux-loss-free routing (book ch. 10, section 10.3.2),
+ *                   added to the softmax probabilities for the choice of
+ *                   the top k only; the gates remain the probabilities. */
 typedef struct grok_moe_args {
   const void* x;
   const void* router_w;
@@ -123,6 +136,8 @@ typedef struct grok_moe_args {
   const void* norm_pre;
   const void* norm_post;
   double norm_eps;
+  int32_t n_shared;
+  const float* router_bias;
 } grok_moe_args;
 
 /* Optional outputs for tests and profiling (every field may be NULL).
@@ -147,10 +162,14 @@ typedef struct grok_moe_debug {
   void* u;
 } grok_moe_debug;
 
-/* Bytes of device workspace grok_moe_forward_ex needs for this shape, or 0 for
- * an invalid or unsupported shape. */
+/* Bytes of device workspace grok_moe_forward_ex needs for this shape without
+ * shared experts, or 0 for an invalid or unsupported shape. */
 size_t grok_moe_workspace_bytes(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t act_dtype,
                                 int32_t w_dtype);
+
+/* The same for a full argument set (counts shared experts); only the shape,
+ * type and n_shared fields are read. 0 for an invalid or unsupported shape. */
+size_t grok_moe_workspace_bytes_ex(const grok_moe_args* a);
 
 /* The layer with caller-owned workspace (ws: device memory, 256-byte aligned,
  * at least grok_moe_workspace_bytes(); its contents on entry do not matter and

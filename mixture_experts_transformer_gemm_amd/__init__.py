@@ -29,8 +29,8 @@ ACT_GELU, ACT_SILU = 0, 1
 OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
 STAGES = ("router", "permute", "gate_up", "down", "combine")
 
-EXPORTED = ("grok_moe_workspace_bytes", "grok_moe_forward_ex", "grok_moe_forward", "grok_moe_forward_w8",
-            "grok_moe_forward_f32", "grok_moe_status_string")
+EXPORTED = ("grok_moe_workspace_bytes", "grok_moe_workspace_bytes_ex", "grok_moe_forward_ex", "grok_moe_forward",
+            "grok_moe_forward_w8", "grok_moe_forward_f32", "grok_moe_status_string")
 
 
 class GrokMoeError(RuntimeError):
@@ -46,7 +46,8 @@ class Args(ctypes.Structure):
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("w_dtype", ctypes.c_int32), ("route_idx", ctypes.c_void_p), ("route_gate", ctypes.c_void_p),
                 ("activation", ctypes.c_int32), ("renormalize", ctypes.c_int32), ("capacity_factor", ctypes.c_double),
-                ("norm_pre", ctypes.c_void_p), ("norm_post", ctypes.c_void_p), ("norm_eps", ctypes.c_double)]
+                ("norm_pre", ctypes.c_void_p), ("norm_post", ctypes.c_void_p), ("norm_eps", ctypes.c_double),
+                ("n_shared", ctypes.c_int32), ("router_bias", ctypes.c_void_p)]
 
 
 class Debug(ctypes.Structure):
@@ -69,6 +70,8 @@ def lib():
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
         h.grok_moe_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, i32]
         h.grok_moe_workspace_bytes.restype = ctypes.c_size_t
+        h.grok_moe_workspace_bytes_ex.argtypes = [ctypes.POINTER(Args)]
+        h.grok_moe_workspace_bytes_ex.restype = ctypes.c_size_t
         h.grok_moe_forward_ex.argtypes = [ctypes.POINTER(Args), vp, ctypes.c_size_t, ctypes.POINTER(Debug), vp]
         h.grok_moe_forward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
         h.grok_moe_forward_w8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
@@ -88,6 +91,12 @@ def grok_moe_status_string(code: int) -> str:
 def grok_moe_workspace_bytes(T: int, d: int, f: int, E: int, k: int, act_dtype: int = BF16,
                              w_dtype: int = BF16) -> int:
     return int(lib().grok_moe_workspace_bytes(T, d, f, E, k, act_dtype, w_dtype))
+
+
+def grok_moe_workspace_bytes_ex(x, router_w, w_gate, w_up, w_down, k: int = 2, **variant) -> int:
+    """Workspace bytes of one grok_moe_forward_ex call with these tensors and variant knobs."""
+    a = make_args(x, router_w, w_gate, w_up, w_down, x, k, **variant)   # out: only its shape is read here
+    return int(lib().grok_moe_workspace_bytes_ex(ctypes.byref(a)))
 
 
 # ---------------------------------------------------------------- torch marshalling
@@ -128,9 +137,11 @@ def _check_tensors(named: Dict[str, object]):
             raise ValueError(f"{name} must be contiguous")
 
 
-def _shape(x, w_gate, router_w):
+def _shape(x, w_gate, router_w, n_shared: int = 0):
+    """(T, d, f, E routed); the weights hold E + n_shared experts."""
     T, d = x.shape
-    E, f, d2 = w_gate.shape
+    Et, f, d2 = w_gate.shape
+    E = Et - n_shared
     if d2 != d:
         raise ValueError(f"w_gate is [E, f, d] with d={d2}, x has d={d}")
     if router_w is not None and tuple(router_w.shape) != (E, d):
@@ -140,17 +151,22 @@ def _shape(x, w_gate, router_w):
 
 def make_args(x, router_w, w_gate, w_up, w_down, out, k: int, scales=None, route_idx=None,
               route_gate=None, activation: int = ACT_GELU, renormalize: bool = False,
-              capacity_factor: float = 0.0, norm_pre=None, norm_post=None, norm_eps: float = 1e-5) -> Args:
-    T, d, f, E = _shape(x, w_gate, router_w)
-    if tuple(w_up.shape) != (E, f, d) or tuple(w_down.shape) != (E, d, f):
-        raise ValueError("w_up must be [E, f, d] and w_down [E, d, f]")
+              capacity_factor: float = 0.0, norm_pre=None, norm_post=None, norm_eps: float = 1e-5,
+              n_shared: int = 0, router_bias=None) -> Args:
+    T, d, f, E = _shape(x, w_gate, router_w, n_shared)
+    Et = E + n_shared
+    if tuple(w_up.shape) != (Et, f, d) or tuple(w_down.shape) != (Et, d, f):
+        raise ValueError("w_up must be [E + n_shared, f, d] and w_down [E + n_shared, d, f]")
+    if router_bias is not None and (tuple(router_bias.shape) != (E,) or router_bias.dtype != _torch().float32):
+        raise ValueError(f"router_bias must be [E] = [{E}] float32")
     if tuple(out.shape) != (T, d):
         raise ValueError("out must be [T, d]")
     for name, g in (("norm_pre", norm_pre), ("norm_post", norm_post)):
         if g is not None and (tuple(g.shape) != (d,) or g.dtype != x.dtype):
             raise ValueError(f"{name} must be [d] = [{d}] of the activation dtype")
     _check_tensors(dict(x=x, router_w=router_w, w_gate=w_gate, w_up=w_up, w_down=w_down, out=out, scales=scales,
-                        route_idx=route_idx, route_gate=route_gate, norm_pre=norm_pre, norm_post=norm_post))
+                        route_idx=route_idx, route_gate=route_gate, norm_pre=norm_pre, norm_post=norm_post,
+                        router_bias=router_bias))
     a = Args()
     a.x, a.router_w, a.w_gate, a.w_up, a.w_down = _ptr(x), _ptr(router_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down)
     a.scales, a.out = _ptr(scales), _ptr(out)
@@ -160,6 +176,7 @@ def make_args(x, router_w, w_gate, w_up, w_down, out, k: int, scales=None, route
     a.route_idx, a.route_gate = _ptr(route_idx), _ptr(route_gate)
     a.activation, a.renormalize, a.capacity_factor = int(activation), int(bool(renormalize)), float(capacity_factor)
     a.norm_pre, a.norm_post, a.norm_eps = _ptr(norm_pre), _ptr(norm_post), float(norm_eps)
+    a.n_shared, a.router_bias = int(n_shared), _ptr(router_bias)
     return a
 
 
@@ -211,20 +228,21 @@ def grok_moe_forward_ex(x, router_w, w_gate, w_up, w_down, k: int = 2, scales=No
                         route_idx=None, route_gate=None, debug: bool = False,
                         events: Optional[Sequence[object]] = None, stream=None, activation: int = ACT_GELU,
                         renormalize: bool = False, capacity_factor: float = 0.0, norm_pre=None, norm_post=None,
-                        norm_eps: float = 1e-5):
+                        norm_eps: float = 1e-5, n_shared: int = 0, router_bias=None):
     """Layer with caller workspace. Returns (out, dbg) where dbg holds the routing intermediates
     (idx, gate, counts, offsets, perm, pos, and u with the sandwich norms) as device tensors when
     debug=True, else {}.
     `events`: up to 6 raw hipEvent_t handles (see `HipEvents`) recorded before each stage and after the last.
     Variants: activation (ACT_GELU / ACT_SILU), renormalize, capacity_factor, norm_pre/norm_post/norm_eps
-    (the sandwich sub-layer out = x + RMSNorm(MoE(RMSNorm(x))))."""
+    (the sandwich sub-layer out = x + RMSNorm(MoE(RMSNorm(x)))), n_shared (shared experts stored after the
+    routed ones in the weights; the debug routing then has k + n_shared slots) and router_bias."""
     torch = _torch()
     dev = x.device
     if out is None:
         out = torch.empty_like(x)
     a = make_args(x, router_w, w_gate, w_up, w_down, out, k, scales, route_idx, route_gate, activation,
-                  renormalize, capacity_factor, norm_pre, norm_post, norm_eps)
-    need = grok_moe_workspace_bytes(a.T, a.d, a.f, a.E, a.k, a.act_dtype, a.w_dtype)
+                  renormalize, capacity_factor, norm_pre, norm_post, norm_eps, n_shared, router_bias)
+    need = int(lib().grok_moe_workspace_bytes_ex(ctypes.byref(a)))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     dbg = {}
@@ -232,13 +250,13 @@ def grok_moe_forward_ex(x, router_w, w_gate, w_up, w_down, k: int = 2, scales=No
     if debug or events:
         d = Debug()
         if debug:
-            T, E = a.T, a.E
-            dbg = dict(idx=torch.full((T, k), -7, dtype=torch.int32, device=dev),
-                       gate=torch.full((T, k), -7.0, dtype=torch.float32, device=dev),
+            T, E, K = a.T, a.E + n_shared, k + n_shared
+            dbg = dict(idx=torch.full((T, K), -7, dtype=torch.int32, device=dev),
+                       gate=torch.full((T, K), -7.0, dtype=torch.float32, device=dev),
                        counts=torch.full((E,), -7, dtype=torch.int32, device=dev),
                        offsets=torch.full((E + 1,), -7, dtype=torch.int32, device=dev),
-                       perm=torch.full((T * k,), -7, dtype=torch.int32, device=dev),
-                       pos=torch.full((T, k), -7, dtype=torch.int32, device=dev))
+                       perm=torch.full((T * K,), -7, dtype=torch.int32, device=dev),
+                       pos=torch.full((T, K), -7, dtype=torch.int32, device=dev))
             if norm_pre is not None:
                 dbg["u"] = torch.empty_like(x)
             for name, t in dbg.items():

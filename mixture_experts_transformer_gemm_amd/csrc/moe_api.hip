@@ -16,25 +16,30 @@ constexpr int64_t kMaxT = int64_t(1) << 20;
 constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int kStream8MaxT = 256;
 constexpr int kStreamMaxT = 64;
+constexpr int kMaxE = 256;       // routed experts
+constexpr int kMaxShared = 4;    // shared experts
+constexpr int kFusedRouterE = 64;  // the one-kernel router's limit
 
 struct Plan {
   int path = 0;
   int mt_max = 1;  // small-M path: rows per expert tile / 16
   int splits = 1;  // split-K factor of the down projection
   int bm = 256;    // tiled path: rows per workgroup tile
+  int rsplits = 0; // split-K factor of the many-expert router GEMM (0: fused router)
   int64_t rows_cap = 0;
   size_t off_idx = 0, off_gate = 0, off_counts = 0, off_offsets = 0, off_perm = 0, off_pos = 0;
-  size_t off_U = 0, off_H = 0, off_Y = 0, total = 0;
+  size_t off_logits = 0, off_U = 0, off_H = 0, off_Y = 0, total = 0;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-int check_shape(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t act, int32_t wdt) {
-  if (T < 0 || d <= 0 || f <= 0 || E < 1 || k < 1 || k > E) return GROK_MOE_EINVAL;
+int check_shape(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns, int32_t act, int32_t wdt) {
+  if (T < 0 || d <= 0 || f <= 0 || E < 1 || k < 1 || k > E || ns < 0) return GROK_MOE_EINVAL;
   const bool combo_ok = (act == GROK_MOE_BF16 && (wdt == GROK_MOE_BF16 || wdt == GROK_MOE_I8)) ||
                         (act == GROK_MOE_F32 && wdt == GROK_MOE_F32);
   if (!combo_ok) return GROK_MOE_EINVAL;
-  if (E > 64 || k > 8 || T > kMaxT || d > kMaxDim || f > kMaxDim) return GROK_MOE_EUNSUPPORTED;
+  if (E > kMaxE || k > 8 || ns > kMaxShared || T > kMaxT || d > kMaxDim || f > kMaxDim) return GROK_MOE_EUNSUPPORTED;
+  if (act == GROK_MOE_F32 && E > kFusedRouterE) return GROK_MOE_EUNSUPPORTED;
   if (act == GROK_MOE_F32) {
     if (d % 8 || f % 4) return GROK_MOE_EUNSUPPORTED;
   } else {
@@ -43,9 +48,12 @@ int check_shape(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t a
   return GROK_MOE_OK;
 }
 
-Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t act, int32_t wdt) {
+// E routed experts, k routed slots, ns shared experts: the kernels see
+// Et = E + ns experts and K = k + ns slots per token.
+Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns, int32_t act, int32_t wdt) {
   Plan p;
-  p.rows_cap = T * k;
+  const int Et = E + ns, K = k + ns;
+  p.rows_cap = T * K;
   if (act == GROK_MOE_F32) {
     p.path = PATH_F32;
   } else if ((wdt == GROK_MOE_BF16 && T <= kStreamMaxT) || (wdt == GROK_MOE_I8 && T <= kStream8MaxT)) {
@@ -55,30 +63,40 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ac
     // each split keeps whole stages (64 bf16 or 128 8-bit reduction values)
     const int64_t ks = wdt == GROK_MOE_I8 ? 128 : 64;
     int s = 1;
-    while (s < 8 && (int64_t)E * (d / 64) * s < 2048 && (f / (2 * s)) % ks == 0) s *= 2;
+    while (s < 8 && (int64_t)Et * (d / 64) * s < 2048 && (f / (2 * s)) % ks == 0) s *= 2;
     p.splits = s;
   } else {
     p.path = PATH_TILED;
-    // about k*T/E rows per expert: the tile height that wastes little of it
-    p.bm = T <= 384 ? 64 : (T <= 1536 ? 128 : 256);
+    // about K*T/Et rows per expert: the tile height that wastes little of it
+    const int64_t r = p.rows_cap / Et;
+    p.bm = r <= 96 ? 64 : (r <= 384 ? 128 : 256);
     // 8-bit weights: one row tile per expert up to 128 rows, so each weight
     // tile is streamed from HBM once
-    if (wdt == GROK_MOE_I8 && T <= 1536) p.bm = 128;
+    if (wdt == GROK_MOE_I8 && r <= 384) p.bm = 128;
     // split the down projection's reduction while its tiles alone would
     // leave CUs idle: (row tiles upper bound) x (d / 256) tiles per split
-    const int64_t tiles = (p.rows_cap / p.bm + E) * (d / 256);
+    const int64_t tiles = (p.rows_cap / p.bm + Et) * (d / 256);
     int s = 1;
     while (s < 8 && tiles * s < 1024 && (f / (2 * s)) % 64 == 0) s *= 2;
     p.splits = s;
   }
+  if (E > kFusedRouterE) {
+    // many-expert router: enough (64 x 64)-tile workgroups, each split a
+    // whole number of 64-wide reduction chunks
+    const int64_t rtiles = ((T + 63) / 64) * ((E + 63) / 64);
+    int s = 1;
+    while (s < 16 && rtiles * s < 256 && (d / 64) % (2 * s) == 0) s *= 2;
+    p.rsplits = s;
+  }
   const size_t hsz = act == GROK_MOE_F32 ? 4 : 2;
   size_t o = 0;
-  p.off_idx = o;     o = align256(o + sizeof(int32_t) * (size_t)(T * k));
-  p.off_gate = o;    o = align256(o + sizeof(float) * (size_t)(T * k));
-  p.off_counts = o;  o = align256(o + sizeof(int32_t) * 64);
-  p.off_offsets = o; o = align256(o + sizeof(int32_t) * 65);
-  p.off_perm = o;    o = align256(o + sizeof(int32_t) * (size_t)(T * k));
-  p.off_pos = o;     o = align256(o + sizeof(int32_t) * (size_t)(T * k));
+  p.off_idx = o;     o = align256(o + sizeof(int32_t) * (size_t)(T * K));
+  p.off_gate = o;    o = align256(o + sizeof(float) * (size_t)(T * K));
+  p.off_counts = o;  o = align256(o + sizeof(int32_t) * (size_t)Et);
+  p.off_offsets = o; o = align256(o + sizeof(int32_t) * (size_t)(Et + 1));
+  p.off_perm = o;    o = align256(o + sizeof(int32_t) * (size_t)(T * K));
+  p.off_pos = o;     o = align256(o + sizeof(int32_t) * (size_t)(T * K));
+  p.off_logits = o;  o = align256(o + sizeof(double) * (size_t)p.rsplits * (size_t)T * (size_t)E);
   p.off_U = o;       o = align256(o + (act == GROK_MOE_F32 ? 4 : 2) * (size_t)T * (size_t)d);  // sandwich pre-norm
   p.off_H = o;       o = align256(o + hsz * (size_t)p.rows_cap * (size_t)f);
   p.off_Y = o;       o = align256(o + sizeof(float) * (size_t)p.splits * (size_t)p.rows_cap * (size_t)d);
@@ -90,7 +108,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 int validate(const grok_moe_args* a) {
   if (!a) return GROK_MOE_EINVAL;
-  int rc = check_shape(a->T, a->d, a->f, a->E, a->k, a->act_dtype, a->w_dtype);
+  int rc = check_shape(a->T, a->d, a->f, a->E, a->k, a->n_shared, a->act_dtype, a->w_dtype);
   if (rc != GROK_MOE_OK || a->T == 0) return rc;
   if (!a->x || !a->out || !a->w_gate || !a->w_up || !a->w_down) return GROK_MOE_EINVAL;
   if (a->route_idx) {
@@ -104,7 +122,7 @@ int validate(const grok_moe_args* a) {
   if ((a->norm_pre == nullptr) != (a->norm_post == nullptr)) return GROK_MOE_EINVAL;
   if (a->norm_pre && (!(a->norm_eps >= 0.0) || !isfinite(a->norm_eps))) return GROK_MOE_EINVAL;
   const void* ptrs[] = {a->x, a->router_w, a->w_gate, a->w_up, a->w_down, a->scales, a->out,
-                        a->route_idx, a->route_gate, a->norm_pre, a->norm_post};
+                        a->route_idx, a->route_gate, a->norm_pre, a->norm_post, a->router_bias};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return GROK_MOE_EALIGN;
   return GROK_MOE_OK;
@@ -139,8 +157,13 @@ extern "C" {
 
 size_t grok_moe_workspace_bytes(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t act_dtype,
                                 int32_t w_dtype) {
-  if (check_shape(T, d, f, E, k, act_dtype, w_dtype) != GROK_MOE_OK) return 0;
-  return make_plan(T, d, f, E, k, act_dtype, w_dtype).total;
+  if (check_shape(T, d, f, E, k, 0, act_dtype, w_dtype) != GROK_MOE_OK) return 0;
+  return make_plan(T, d, f, E, k, 0, act_dtype, w_dtype).total;
+}
+
+size_t grok_moe_workspace_bytes_ex(const grok_moe_args* a) {
+  if (!a || check_shape(a->T, a->d, a->f, a->E, a->k, a->n_shared, a->act_dtype, a->w_dtype) != GROK_MOE_OK) return 0;
+  return make_plan(a->T, a->d, a->f, a->E, a->k, a->n_shared, a->act_dtype, a->w_dtype).total;
 }
 
 int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const grok_moe_debug* dbg,
@@ -148,7 +171,7 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
   int rc = validate(a);
   if (rc != GROK_MOE_OK) return rc;
   if (a->T == 0) return GROK_MOE_OK;
-  const Plan p = make_plan(a->T, a->d, a->f, a->E, a->k, a->act_dtype, a->w_dtype);
+  const Plan p = make_plan(a->T, a->d, a->f, a->E, a->k, a->n_shared, a->act_dtype, a->w_dtype);
   if (!ws || ws_bytes < p.total) return GROK_MOE_EWORKSPACE;
   if (((uintptr_t)ws & 255) != 0) return GROK_MOE_EALIGN;
 
@@ -160,11 +183,15 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
   int32_t* offsets = (int32_t*)(w + p.off_offsets);
   int32_t* perm = (int32_t*)(w + p.off_perm);
   int32_t* pos = (int32_t*)(w + p.off_pos);
+  double* logits = (double*)(w + p.off_logits);
   void* U = w + p.off_U;
   void* H = w + p.off_H;
   float* Y = (float*)(w + p.off_Y);
   const int64_t T = a->T;
-  const int d = (int)a->d, f = (int)a->f, E = a->E, k = a->k;
+  // E routed experts and k routed slots; with the ns shared experts the
+  // kernels after the router see Et experts and K slots per token
+  const int d = (int)a->d, f = (int)a->f, Er = a->E, kr = a->k, ns = a->n_shared;
+  const int E = Er + ns, k = kr + ns;
   const int act_f32 = a->act_dtype == GROK_MOE_F32;
   const int w8 = a->w_dtype == GROK_MOE_I8;
   const int sandwich = a->norm_pre != nullptr;
@@ -180,14 +207,22 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
   const int32_t* ridx = idx;
   const float* rgate = gate;
   if (a->route_idx) {
-    ridx = a->route_idx;
-    rgate = a->route_gate;
+    if (ns == 0) {
+      ridx = a->route_idx;
+      rgate = a->route_gate;
+    } else {
+      GMOE_TRY(launch_append_shared(a->route_idx, a->route_gate, T, Er, kr, ns, idx, gate, st));
+    }
+  } else if (p.rsplits == 0) {
+    GMOE_TRY(launch_router(act_f32, A, a->router_w, T, d, Er, kr, ns, a->renormalize != 0, a->router_bias, idx, gate,
+                           st));
   } else {
-    GMOE_TRY(launch_router(act_f32, A, a->router_w, T, d, E, k, a->renormalize != 0, idx, gate, st));
+    GMOE_TRY(launch_router_many((const bf16_bits*)A, (const bf16_bits*)a->router_w, T, d, Er, kr, ns,
+                                a->renormalize != 0, a->router_bias, p.rsplits, logits, idx, gate, st));
   }
-  // stage 1: permutation (with the capacity cap)
+  // stage 1: permutation (with the capacity cap on the routed experts)
   if (!record(dbg, 1, st)) return GROK_MOE_EHIP;
-  GMOE_TRY(launch_permute(ridx, T, E, k, capacity_rows(a->capacity_factor, T, E, k), counts, offsets, perm, pos,
+  GMOE_TRY(launch_permute(ridx, T, E, k, capacity_rows(a->capacity_factor, T, Er, kr), Er, counts, offsets, perm, pos,
                           st));
   const RouteView rv{counts, offsets, perm};
 
@@ -239,7 +274,7 @@ static int forward_alloc(const grok_moe_args* a, void* stream) {
   int rc = validate(a);
   if (rc != GROK_MOE_OK) return rc;
   if (a->T == 0) return GROK_MOE_OK;
-  const size_t bytes = grok_moe_workspace_bytes(a->T, a->d, a->f, a->E, a->k, a->act_dtype, a->w_dtype);
+  const size_t bytes = grok_moe_workspace_bytes_ex(a);
   hipStream_t st = (hipStream_t)stream;
   void* ws = nullptr;
   if (hipMallocAsync(&ws, bytes, st) != hipSuccess) return GROK_MOE_EHIP;
@@ -285,7 +320,9 @@ const char* grok_moe_status_string(int status) {
   switch (status) {
     case GROK_MOE_OK: return "ok";
     case GROK_MOE_EINVAL: return "invalid argument (null pointer, negative size, k > E or bad dtype)";
-    case GROK_MOE_EUNSUPPORTED: return "unsupported shape (E <= 64, k <= 8, d % 256 == 0, f % 256 == 0 for bf16/int8)";
+    case GROK_MOE_EUNSUPPORTED:
+      return "unsupported shape (E <= 256 (64 for fp32), k <= 8, n_shared <= 4, d % 256 == 0, f % 256 == 0 for "
+             "bf16/int8)";
     case GROK_MOE_EALIGN: return "misaligned pointer (16-byte tensors, 256-byte workspace)";
     case GROK_MOE_EWORKSPACE: return "workspace missing or too small";
     case GROK_MOE_EHIP: return "HIP runtime call failed";

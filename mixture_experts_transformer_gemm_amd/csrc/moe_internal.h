@@ -48,13 +48,28 @@ struct RouteView {
 // ---------------------------------------------------------------- launchers
 // All launchers enqueue on `stream` and return the launch status.
 
-// renorm: divide the k selected gates by their sum.
-hipError_t launch_router(int act_f32, const void* x, const void* router_w, int64_t T, int d, int E, int k,
-                         int renorm, int32_t* idx, float* gate, hipStream_t stream);
+// Routing over E <= 64 experts in one kernel. Writes idx/gate [T][k + ns]:
+// the k routed slots, then the ns shared experts E.. with gate 1.
+// renorm: divide the k selected gates by their sum. bias (nullable, [E]):
+// added to the probabilities for the choice only.
+hipError_t launch_router(int act_f32, const void* x, const void* router_w, int64_t T, int d, int E, int k, int ns,
+                         int renorm, const float* bias, int32_t* idx, float* gate, hipStream_t stream);
 
-// cap >= 0: an expert keeps its first `cap` assignments in token order, the
-// others get pos = -1 and no row; cap < 0: no cap.
-hipError_t launch_permute(const int32_t* idx, int64_t T, int E, int k, int64_t cap, int32_t* counts,
+// The same for E > 64 (bf16): split-K fp64 logit GEMM into P [splits][T][E],
+// then one wavefront per token for softmax and top-k. d / splits must be a
+// multiple of 64.
+hipError_t launch_router_many(const bf16_bits* x, const bf16_bits* router_w, int64_t T, int d, int E, int k, int ns,
+                              int renorm, const float* bias, int splits, double* P, int32_t* idx, float* gate,
+                              hipStream_t stream);
+
+// Caller routing [T][k] -> idx/gate [T][k + ns] with the shared slots.
+hipError_t launch_append_shared(const int32_t* ridx, const float* rgate, int64_t T, int E, int k, int ns,
+                                int32_t* idx, float* gate, hipStream_t stream);
+
+// E experts, k slots per token. cap >= 0: an expert e < E_cap keeps its
+// first `cap` assignments in token order, the others get pos = -1 and no
+// row; cap < 0: no cap. E <= 272, k <= 12.
+hipError_t launch_permute(const int32_t* idx, int64_t T, int E, int k, int64_t cap, int E_cap, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t stream);
 
 // out[t] = sum_s gate[t][s] * (sum_{p<S} Y[p][pos[t][s]]), Y: [S][rows_cap][d] fp32

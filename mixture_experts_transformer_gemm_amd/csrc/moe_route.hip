@@ -44,10 +44,14 @@ __device__ __forceinline__ void load8_f64(const float* p, double* o) {
 // accumulates 8 experts at a time over its 8-element chunks; the partials are
 // summed across lanes (butterfly) and across the 4 wavefronts (LDS, fixed
 // order). Wavefront 0 then holds logit e in lane e; softmax and the k-fold
-// arg-max run across its lanes.
+// arg-max run across its lanes. E <= 64.
+// Output rows have K = k + ns slots: the k routed ones, then the ns shared
+// experts E .. E+ns-1 with gate 1. bias (nullable): added to p for the
+// choice only (the aux-loss-free routing bias, book ch. 10, section 10.3.2).
 template <typename XT>
 __global__ __launch_bounds__(256) void router_topk_kernel(const XT* __restrict__ x, const XT* __restrict__ wr,
-                                                          int64_t T, int d, int E, int k, int renorm,
+                                                          int64_t T, int d, int E, int k, int ns, int renorm,
+                                                          const float* __restrict__ bias,
                                                           int32_t* __restrict__ idx, float* __restrict__ gate) {
   __shared__ double s_part[4][64];
   const int lane = threadIdx.x & 63;
@@ -86,6 +90,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const XT* __restrict__
       const double ex = live ? exp(my_logit - mx) : 0.0;
       const double z = wave_sum_f64(ex);
       const double p = ex / z;
+      const double key = live ? p + (bias ? (double)bias[lane] : 0.0) : -INFINITY;
       bool taken = false;
       double gsel[8];
       int isel[8];
@@ -94,20 +99,20 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const XT* __restrict__
         gsel[s] = 0.0;
         isel[s] = 0;
         if (s < k) {
-          // arg-max of p over the experts not yet taken; key (p desc, index asc)
-          double pv = (live && !taken) ? p : -1.0;
+          // arg-max over the experts not yet taken; key (p + bias desc, index asc)
+          double kv = (live && !taken) ? key : -INFINITY;
           int bi = lane;
 #pragma unroll
           for (int off = 32; off > 0; off >>= 1) {
-            const double po = __shfl_xor(pv, off, 64);
+            const double ko = __shfl_xor(kv, off, 64);
             const int io = __shfl_xor(bi, off, 64);
-            if (po > pv || (po == pv && io < bi)) {
-              pv = po;
+            if (ko > kv || (ko == kv && io < bi)) {
+              kv = ko;
               bi = io;
             }
           }
           if (lane == bi) taken = true;
-          gsel[s] = pv;
+          gsel[s] = __shfl(p, bi, 64);  // the gate is the probability itself
           isel[s] = bi;
         }
       }
@@ -116,29 +121,245 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const XT* __restrict__
         double sum = 0.0;
 #pragma unroll
         for (int s = 0; s < 8; ++s) sum += gsel[s];
+        const int K = k + ns;
 #pragma unroll
         for (int s = 0; s < 8; ++s)
           if (s < k) {
-            idx[t * k + s] = isel[s];
-            gate[t * k + s] = (float)(renorm ? gsel[s] / sum : gsel[s]);
+            idx[t * K + s] = isel[s];
+            gate[t * K + s] = (float)(renorm ? gsel[s] / sum : gsel[s]);
           }
+        for (int j = 0; j < ns; ++j) {
+          idx[t * K + k + j] = E + j;
+          gate[t * K + k + j] = 1.0f;
+        }
       }
     }
     __syncthreads();
   }
 }
 
-hipError_t launch_router(int act_f32, const void* x, const void* router_w, int64_t T, int d, int E, int k,
-                         int renorm, int32_t* idx, float* gate, hipStream_t stream) {
+hipError_t launch_router(int act_f32, const void* x, const void* router_w, int64_t T, int d, int E, int k, int ns,
+                         int renorm, const float* bias, int32_t* idx, float* gate, hipStream_t stream) {
   int64_t blocks = T;
   if (blocks > 16384) blocks = 16384;
   if (blocks < 1) blocks = 1;
   if (act_f32)
     hipLaunchKernelGGL(router_topk_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const float*)x, (const float*)router_w, T, d, E, k, renorm, idx, gate);
+                       (const float*)x, (const float*)router_w, T, d, E, k, ns, renorm, bias, idx, gate);
   else
     hipLaunchKernelGGL(router_topk_kernel<bf16_bits>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const bf16_bits*)x, (const bf16_bits*)router_w, T, d, E, k, renorm, idx, gate);
+                       (const bf16_bits*)x, (const bf16_bits*)router_w, T, d, E, k, ns, renorm, bias, idx, gate);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- many-expert router (E > 64)
+// Fine-grained layers route over hundreds of experts (256 in DeepSeek-V3,
+// book ch. 10, section 10.1 table). The logits become a [T][E] GEMM in two
+// kernels: router_gemm_kernel forms split-K partial logits in fp64 (each
+// bf16 product is exact in fp64), router_topk_wave_kernel sums the partials
+// in split order and runs softmax and top-k with one wavefront per token.
+
+// Workgroup tile: 64 tokens x 64 experts, reduction chunks of 64 staged as
+// bf16 in LDS (rows padded to 72 values, so the 16 rows that a wavefront
+// reads at once fall into distinct banks). Thread (tm, tn) owns tokens
+// tm + 16i and experts tn + 16j (i, j < 4); grid z splits the reduction.
+constexpr int kRgTile = 64, kRgK = 64, kRgLd = kRgK + 8;
+
+__device__ __forceinline__ void bf16x8_to_f64(uint4 v, double* o) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = (double)__uint_as_float(w[i] << 16);
+    o[2 * i + 1] = (double)__uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+__global__ __launch_bounds__(256) void router_gemm_kernel(const bf16_bits* __restrict__ x,
+                                                          const bf16_bits* __restrict__ wr, int64_t T, int d, int E,
+                                                          double* __restrict__ P) {
+  __shared__ __attribute__((aligned(16))) bf16_bits sx[kRgTile * kRgLd];
+  __shared__ __attribute__((aligned(16))) bf16_bits sw[kRgTile * kRgLd];
+  const int tid = threadIdx.x, tn = tid & 15, tm = tid >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * kRgTile;
+  const int e0 = blockIdx.y * kRgTile;
+  const int kspan = d / (int)gridDim.z, kbeg = (int)blockIdx.z * kspan;
+  double acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  for (int kc = kbeg; kc < kbeg + kspan; kc += kRgK) {
+    // 64 rows x 64 values of each operand: 512 16-byte pieces, 2 per thread
+    uint4 vx[2], vw[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int lin = tid + 256 * q, r = lin >> 3, c = (lin & 7) * 8;
+      const int64_t tok = t0 + r;
+      const int e = e0 + r;
+      vx[q] = tok < T ? *reinterpret_cast<const uint4*>(x + tok * d + kc + c) : make_uint4(0, 0, 0, 0);
+      vw[q] = e < E ? *reinterpret_cast<const uint4*>(wr + (int64_t)e * d + kc + c) : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int lin = tid + 256 * q, r = lin >> 3, c = (lin & 7) * 8;
+      *reinterpret_cast<uint4*>(sx + r * kRgLd + c) = vx[q];
+      *reinterpret_cast<uint4*>(sw + r * kRgLd + c) = vw[q];
+    }
+    __syncthreads();
+#pragma unroll 2
+    for (int k8 = 0; k8 < kRgK; k8 += 8) {
+      double xv[4][8], wv[4][8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bf16x8_to_f64(*reinterpret_cast<const uint4*>(sx + (tm + 16 * i) * kRgLd + k8), xv[i]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bf16x8_to_f64(*reinterpret_cast<const uint4*>(sw + (tn + 16 * j) * kRgLd + k8), wv[j]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = fma(xv[i][q], wv[j][q], acc[i][j]);
+    }
+  }
+  double* Ps = P + (int64_t)blockIdx.z * T * E;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t tok = t0 + tm + 16 * i;
+    if (tok >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tn + 16 * j;
+      if (e < E) Ps[tok * E + e] = acc[i][j];
+    }
+  }
+}
+
+// One wavefront per token; lane l holds experts l, l + 64, l + 128, l + 192.
+__global__ __launch_bounds__(256) void router_topk_wave_kernel(const double* __restrict__ P, int S, int64_t T, int E,
+                                                               int k, int ns, int renorm,
+                                                               const float* __restrict__ bias,
+                                                               int32_t* __restrict__ idx, float* __restrict__ gate) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int K = k + ns;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t < T; t += (int64_t)gridDim.x * 4) {
+    double lg[4], p[4], key[4];
+    bool live[4], taken[4];
+    double mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      live[j] = e < E;
+      taken[j] = false;
+      lg[j] = 0.0;
+      if (live[j])
+        for (int s = 0; s < S; ++s) lg[j] += P[((int64_t)s * T + t) * E + e];
+      if (live[j]) mx = fmax(mx, lg[j]);
+    }
+    mx = wave_max_f64(mx);
+    double zs = 0.0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = live[j] ? exp(lg[j] - mx) : 0.0;
+      zs += p[j];
+    }
+    const double z = wave_sum_f64(zs);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = p[j] / z;
+      key[j] = live[j] ? p[j] + (bias ? (double)bias[lane + 64 * j] : 0.0) : -INFINITY;
+    }
+    double gsel[8];
+    int isel[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      gsel[s] = 0.0;
+      isel[s] = 0;
+      if (s < k) {
+        // this lane's best untaken expert, then the wavefront's; key (p + bias desc, index asc)
+        double kv = -INFINITY, pv = 0.0;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = lane + 64 * j;
+          if (live[j] && !taken[j] && (key[j] > kv || (key[j] == kv && e < bi))) {
+            kv = key[j];
+            pv = p[j];
+            bi = e;
+          }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+          const double ko = __shfl_xor(kv, off, 64);
+          const double po = __shfl_xor(pv, off, 64);
+          const int io = __shfl_xor(bi, off, 64);
+          if (ko > kv || (ko == kv && io < bi)) {
+            kv = ko;
+            pv = po;
+            bi = io;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (lane + 64 * j == bi) taken[j] = true;
+        gsel[s] = pv;
+        isel[s] = bi;
+      }
+    }
+    if (lane == 0) {
+      double sum = 0.0;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) sum += gsel[s];
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        if (s < k) {
+          idx[t * K + s] = isel[s];
+          gate[t * K + s] = (float)(renorm ? gsel[s] / sum : gsel[s]);
+        }
+      for (int j = 0; j < ns; ++j) {
+        idx[t * K + k + j] = E + j;
+        gate[t * K + k + j] = 1.0f;
+      }
+    }
+  }
+}
+
+hipError_t launch_router_many(const bf16_bits* x, const bf16_bits* router_w, int64_t T, int d, int E, int k, int ns,
+                              int renorm, const float* bias, int splits, double* P, int32_t* idx, float* gate,
+                              hipStream_t stream) {
+  const dim3 grid((unsigned)((T + kRgTile - 1) / kRgTile), (unsigned)((E + kRgTile - 1) / kRgTile), (unsigned)splits);
+  hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(256), 0, stream, x, router_w, T, d, E, P);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  int64_t blocks = (T + 3) / 4;
+  if (blocks > 16384) blocks = 16384;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(router_topk_wave_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, P, splits, T, E, k, ns,
+                     renorm, bias, idx, gate);
+  return hipGetLastError();
+}
+
+// Caller-given routing [T][k] plus the ns shared slots -> [T][k + ns].
+__global__ __launch_bounds__(256) void append_shared_kernel(const int32_t* __restrict__ ridx,
+                                                            const float* __restrict__ rgate, int64_t T, int E, int k,
+                                                            int ns, int32_t* __restrict__ idx,
+                                                            float* __restrict__ gate) {
+  const int K = k + ns;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < T * K; i += (int64_t)gridDim.x * 256) {
+    const int64_t t = i / K;
+    const int s = (int)(i - t * K);
+    idx[i] = s < k ? ridx[t * k + s] : E + (s - k);
+    gate[i] = s < k ? rgate[t * k + s] : 1.0f;
+  }
+}
+
+hipError_t launch_append_shared(const int32_t* ridx, const float* rgate, int64_t T, int E, int k, int ns,
+                                int32_t* idx, float* gate, hipStream_t stream) {
+  int64_t blocks = (T * (k + ns) + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(append_shared_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ridx, rgate, T, E, k, ns,
+                     idx, gate);
   return hipGetLastError();
 }
 
@@ -152,35 +373,43 @@ hipError_t launch_router(int act_f32, const void* x, const void* router_w, int64
 // A token that lists an expert twice is counted once (both slots then point
 // at the same row); indices outside [0, E) are dropped (pos = -1).
 // With a capacity (cap >= 0; book ch. 10, section 10.3.2, the capacity
-// factor box) an expert's assignments of rank >= cap in token order are
-// dropped too: pos = -1, no row, and the segment holds the first cap.
+// factor box) an assignment to a capped expert (e < E_cap: the routed ones)
+// of rank >= cap in token order is dropped too: pos = -1, no row, and the
+// segment holds the first cap.
+constexpr int kPermMaxE = 272;  // routed + shared experts
+constexpr int kPermMaxK = 12;   // slots per token
 __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ idx, int64_t T, int E, int k,
-                                                       int64_t cap, int32_t* __restrict__ counts,
+                                                       int64_t cap, int E_cap, int32_t* __restrict__ counts,
                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                        int32_t* __restrict__ pos) {
-  __shared__ int s_cnt[64];
-  __shared__ int s_base[64];  // assignments of expert e in the chunks already walked
-  __shared__ int s_off[64];   // first row of segment e
-  __shared__ int s_lim[64];   // rows segment e keeps
-  __shared__ int s_wave[16][64];
+  __shared__ int s_cnt[kPermMaxE];
+  __shared__ int s_base[kPermMaxE];  // assignments of expert e in the chunks already walked
+  __shared__ int s_off[kPermMaxE];   // first row of segment e
+  __shared__ int s_lim[kPermMaxE];   // rows segment e keeps
+  __shared__ int s_wave[16][kPermMaxE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < 64) s_cnt[tid] = 0;
+  if (tid < kPermMaxE) s_cnt[tid] = 0;
   __syncthreads();
   for (int64_t t = tid; t < T; t += 1024) {
-    int es[8];
-    for (int s = 0; s < k; ++s) {
-      int e = idx[t * k + s];
-      bool ok = e >= 0 && e < E;
-      for (int q = 0; q < s; ++q) ok = ok && es[q] != e;
-      es[s] = e;
-      if (ok) atomicAdd(&s_cnt[e], 1);
+    int es[kPermMaxK];
+#pragma unroll
+    for (int s = 0; s < kPermMaxK; ++s) {
+      es[s] = -1;
+      if (s < k) {
+        const int e = idx[t * k + s];
+        bool ok = e >= 0 && e < E;
+#pragma unroll
+        for (int q = 0; q < s; ++q) ok = ok && es[q] != e;
+        es[s] = e;
+        if (ok) atomicAdd(&s_cnt[e], 1);
+      }
     }
   }
   __syncthreads();
   if (tid == 0) {
     int acc = 0;
     for (int e = 0; e < E; ++e) {
-      const int c = (cap >= 0 && (int64_t)s_cnt[e] > cap) ? (int)cap : s_cnt[e];
+      const int c = (cap >= 0 && e < E_cap && (int64_t)s_cnt[e] > cap) ? (int)cap : s_cnt[e];
       offsets[e] = acc;
       counts[e] = c;
       s_off[e] = acc;
@@ -194,28 +423,32 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t t0 = 0; t0 < T; t0 += 1024) {
     const int64_t t = t0 + tid;
-    int my_e[8], my_rank[8];
-    for (int s = 0; s < 8; ++s) {
+    int my_e[kPermMaxK], my_rank[kPermMaxK];
+#pragma unroll
+    for (int s = 0; s < kPermMaxK; ++s) {
       my_e[s] = -1;
       my_rank[s] = 0;
-    }
-    if (t < T)
-      for (int s = 0; s < k; ++s) {
-        int e = idx[t * k + s];
+      if (t < T && s < k) {
+        const int e = idx[t * k + s];
         my_e[s] = (e >= 0 && e < E) ? e : -1;
       }
+    }
     for (int e = 0; e < E; ++e) {
       bool sel = false;
-      for (int s = 0; s < k; ++s) sel = sel || (my_e[s] == e);
+#pragma unroll
+      for (int s = 0; s < kPermMaxK; ++s) sel = sel || (my_e[s] == e);
       const uint64_t m = __ballot(sel);
       if (lane == 0) s_wave[wave][e] = __popcll(m);
       const int r = __popcll(m & lt_mask);
-      for (int s = 0; s < k; ++s)
+#pragma unroll
+      for (int s = 0; s < kPermMaxK; ++s)
         if (my_e[s] == e) my_rank[s] = r;
     }
     __syncthreads();
     if (t < T) {
-      for (int s = 0; s < k; ++s) {
+#pragma unroll
+      for (int s = 0; s < kPermMaxK; ++s) {
+        if (s >= k) break;
         const int e = my_e[s];
         int row = -1;
         if (e >= 0) {
@@ -240,9 +473,10 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
   }
 }
 
-hipError_t launch_permute(const int32_t* idx, int64_t T, int E, int k, int64_t cap, int32_t* counts,
+hipError_t launch_permute(const int32_t* idx, int64_t T, int E, int k, int64_t cap, int E_cap, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t stream) {
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, stream, idx, T, E, k, cap, counts, offsets, perm,
+  if (E > kPermMaxE || k > kPermMaxK) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, stream, idx, T, E, k, cap, E_cap, counts, offsets, perm,
                      pos);
   return hipGetLastError();
 }

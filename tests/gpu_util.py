@@ -22,7 +22,7 @@ def to_dev(a, torch):
 
 def dev_workload(w: synthetic.Workload, torch):
     return {n: to_dev(getattr(w, n), torch)
-            for n in ("x", "router_w", "w_gate", "w_up", "w_down", "scales", "norm_pre", "norm_post")}
+            for n in ("x", "router_w", "w_gate", "w_up", "w_down", "scales", "norm_pre", "norm_post", "router_bias")}
 
 
 def run_layer(w: synthetic.Workload, torch, dev=None, route_idx=None, route_gate=None, debug=True):
@@ -35,7 +35,8 @@ def run_layer(w: synthetic.Workload, torch, dev=None, route_idx=None, route_gate
                                       k=w.k, scales=dev["scales"], route_idx=ri, route_gate=rg, debug=debug,
                                       activation=gm.ACT_SILU if w.activation == "silu" else gm.ACT_GELU,
                                       renormalize=w.renormalize, capacity_factor=w.capacity_factor,
-                                      norm_pre=dev["norm_pre"], norm_post=dev["norm_post"], norm_eps=w.norm_eps)
+                                      norm_pre=dev["norm_pre"], norm_post=dev["norm_post"], norm_eps=w.norm_eps,
+                                      n_shared=w.n_shared, router_bias=dev["router_bias"])
     torch.cuda.synchronize()
     got = out.float().cpu().numpy().astype(np.float64)
     host = {}

@@ -53,7 +53,10 @@ def test_workspace_bytes():
     # invalid / unsupported shapes report 0
     assert gm.grok_moe_workspace_bytes(8, 6144, 32768, 8, 9) == 0          # k > E
     assert gm.grok_moe_workspace_bytes(8, 6100, 32768, 8, 2) == 0          # d % 128
-    assert gm.grok_moe_workspace_bytes(8, 6144, 32768, 65, 2) == 0         # E > 64
+    assert gm.grok_moe_workspace_bytes(8, 6144, 32768, 257, 2) == 0        # E > 256
+    assert gm.grok_moe_workspace_bytes(8, 64, 64, 65, 2, gm.F32, gm.F32) == 0   # fp32 router: E <= 64
+    # many experts: the router's split-K logits [S][T][E] fp64 are part of the workspace
+    assert gm.grok_moe_workspace_bytes(8192, 7168, 2048, 256, 8) >= 8192 * 256 * 8
     assert gm.grok_moe_workspace_bytes(8, 6144, 32768, 8, 2, gm.F32, gm.BF16) == 0   # dtype combo
 
 
@@ -62,7 +65,7 @@ def _args(**kw):
     base = dict(x=0x10000, router_w=0x20000, w_gate=0x30000, w_up=0x40000, w_down=0x50000, scales=None,
                 out=0x60000, T=8, d=256, f=512, E=8, k=2, act_dtype=gm.BF16, w_dtype=gm.BF16, route_idx=None,
                 route_gate=None, activation=gm.ACT_GELU, renormalize=0, capacity_factor=0.0, norm_pre=None,
-                norm_post=None, norm_eps=1e-5)
+                norm_post=None, norm_eps=1e-5, n_shared=0, router_bias=None)
     base.update(kw)
     for n, v in base.items():
         setattr(a, n, v)
@@ -87,8 +90,12 @@ def _call(a, ws=0x1000000, ws_bytes=1 << 40):
     (dict(act_dtype=gm.F32), gm.EINVAL),             # f32 activations with bf16 weights
     (dict(act_dtype=5), gm.EINVAL),
     (dict(w_dtype=gm.I8), gm.EINVAL),                # int8 without scales
-    (dict(E=65, k=2), gm.EUNSUPPORTED),
+    (dict(E=257, k=2), gm.EUNSUPPORTED),
+    (dict(E=65, k=2, act_dtype=gm.F32, w_dtype=gm.F32), gm.EUNSUPPORTED),
     (dict(E=16, k=9), gm.EUNSUPPORTED),
+    (dict(n_shared=5), gm.EUNSUPPORTED),
+    (dict(n_shared=-1), gm.EINVAL),
+    (dict(router_bias=0x80004), gm.EALIGN),
     (dict(d=200), gm.EUNSUPPORTED),
     (dict(d=384), gm.EUNSUPPORTED),
     (dict(f=384), gm.EUNSUPPORTED),
@@ -115,8 +122,21 @@ def test_validation_errors(kw, code):
 def test_variant_arguments_reach_the_workspace_check():
     # valid variant knobs pass validation (the call then stops at the missing workspace)
     for kw in (dict(activation=gm.ACT_SILU, renormalize=1), dict(capacity_factor=1.25),
-               dict(norm_pre=0x80000, norm_post=0x90000, norm_eps=0.0)):
+               dict(norm_pre=0x80000, norm_post=0x90000, norm_eps=0.0), dict(n_shared=4),
+               dict(E=256, k=8, n_shared=1, router_bias=0x80000)):
         assert _call(_args(**kw), ws=0, ws_bytes=0) == gm.EWORKSPACE
+
+
+def test_workspace_bytes_ex_counts_shared_experts():
+    a = _args(T=64, d=7168, f=2048, E=256, k=8)
+    base = gm.lib().grok_moe_workspace_bytes_ex(ctypes.byref(a))
+    assert base == gm.grok_moe_workspace_bytes(64, 7168, 2048, 256, 8)
+    a.n_shared = 1
+    more = gm.lib().grok_moe_workspace_bytes_ex(ctypes.byref(a))
+    assert more >= base + 64 * 2048 * 2          # one more H row per token at least
+    assert _call(a, ws=0x1000000, ws_bytes=base) == gm.EWORKSPACE
+    a.k = 9
+    assert gm.lib().grok_moe_workspace_bytes_ex(ctypes.byref(a)) == 0
 
 
 def test_ctypes_structs_match_the_header(tmp_path):

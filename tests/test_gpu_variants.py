@@ -1,8 +1,10 @@
 """GPU parity of the layer variants against the CPU oracle (``oracle.layer``):
 SiLU experts with renormalised gates (the Mixtral variant), capacity-factor
-drops, and the sandwich sub-layer (RMSNorm before and after the MoE, plus the
-residual), on the bf16, 8-bit and fp32 paths, small shapes spanning the
-weight-streaming and tiled kernels, and at full Mixtral 8x22B / Grok-1 sizes.
+drops, the sandwich sub-layer (RMSNorm before and after the MoE, plus the
+residual) and the fine-grained layout (up to 256 routed experts, top-8, a
+selection bias, shared experts), on the bf16, 8-bit and fp32 paths, small
+shapes spanning the weight-streaming and tiled kernels, and at full Mixtral
+8x22B / Grok-1 / DeepSeek-V3 sizes.
 
 Rules as in the other parity tests: routing indices equal the oracle's; the
 permutation (with dropped assignments at pos = -1) is bit-exact against the
@@ -28,7 +30,8 @@ def _oracle(w, tokens=None):
     return oracle.layer(w.x, w.router_w, w.w_gate, w.w_up, w.w_down, w.k, scales=w.scales,
                         activation=oracle.SILU if w.activation == "silu" else oracle.GELU,
                         renormalize=w.renormalize, capacity_factor=w.capacity_factor, norm_pre=w.norm_pre,
-                        norm_post=w.norm_post, norm_eps=w.norm_eps, tokens=tokens)
+                        norm_post=w.norm_post, norm_eps=w.norm_eps, n_shared=w.n_shared,
+                        router_bias=w.router_bias, tokens=tokens)
 
 
 def _tol(w):
@@ -36,9 +39,9 @@ def _tol(w):
 
 
 def _check(w, tokens=None, label=""):
-    print(f"[variants] {label} T={w.T} d={w.d} f={w.f} E={w.E} k={w.k} act={w.activation} "
+    print(f"[variants] {label} T={w.T} d={w.d} f={w.f} E={w.E}+{w.n_shared} k={w.k} act={w.activation} "
           f"renorm={w.renormalize} cap={w.capacity_factor} sandwich={w.norm_pre is not None} "
-          f"w={w.w_dtype}", flush=True)
+          f"bias={w.router_bias is not None} w={w.w_dtype}", flush=True)
     got, dbg = run_layer(w, torch)
     ref = _oracle(w, tokens=tokens)
     if w.norm_pre is not None:
@@ -47,9 +50,9 @@ def _check(w, tokens=None, label=""):
     gate_tol = 1e-6 * np.maximum(ref["gate"], 1e-30) + 1e-12
     assert np.all(np.abs(dbg["gate"].astype(np.float64) - ref["gate"]) <= gate_tol)
     if w.renormalize:
-        np.testing.assert_allclose(dbg["gate"].sum(axis=1), 1.0, atol=1e-6)
+        np.testing.assert_allclose(dbg["gate"][:, :w.k].sum(axis=1), 1.0, atol=1e-6)
     cap = oracle.capacity(w.capacity_factor, w.T, w.E, w.k)
-    c, o, p, pos = oracle.permute_cap(dbg["idx"], w.E, cap)
+    c, o, p, pos = oracle.permute_cap(dbg["idx"], w.E + w.n_shared, cap, E_cap=w.E)
     np.testing.assert_array_equal(dbg["counts"], c)
     np.testing.assert_array_equal(dbg["offsets"], o)
     np.testing.assert_array_equal(dbg["perm"][:o[-1]], p[:o[-1]])
@@ -191,6 +194,74 @@ def test_capacity_skew_full_sampled():
     ref = _oracle(w, tokens=toks)
     err = normwise_err(got[toks], ref["out"])
     print(f"[variants] capacity skew full: {len(toks)} tokens, normwise error {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+    del w
+    gc.collect()
+
+
+# ---------------------------------------------------------------- fine-grained: many experts, bias, shared experts
+@pytest.mark.parametrize("T,E", [(1, 256), (8, 256), (64, 256), (300, 256), (1000, 256), (40, 72), (200, 100)])
+def test_fine_grained_bf16(T, E):
+    # E > 64: the split-K fp64 router GEMM + one-wavefront top-k; top-8, one shared expert, selection bias
+    w = synthetic.make("dsv3_decode", T=T, d=256, f=256, E=E, seed=400 + T)
+    got, dbg, _ = _check(w, label="fine-grained")
+    assert (dbg["idx"][:, 8] == E).all() and (dbg["gate"][:, 8] == 1.0).all()
+    assert dbg["counts"][E] == T                      # the shared expert runs every token
+
+
+def test_fine_grained_fused_router_two_shared():
+    # E <= 64 keeps the one-kernel router; bias and two shared experts
+    w = synthetic.make("dsv3_decode", T=90, d=256, f=256, E=32, k=4, n_shared=2, seed=5)
+    _check(w, label="E=32 two shared")
+
+
+def test_fine_grained_int8_and_capacity():
+    w = synthetic.make("dsv3_decode", T=120, d=256, f=256, seed=6, w_dtype="i8")
+    w.scales = synthetic.random_scales(w.E + w.n_shared, w.d, w.f, seed=6)
+    _check(w, label="fine-grained int8")
+    w = synthetic.make("dsv3_decode", T=400, d=256, f=256, seed=7, capacity_factor=0.5, skew=True)
+    got, dbg, _ = _check(w, label="fine-grained capacity")
+    assert (dbg["pos"][:, :8] == -1).any() and (dbg["pos"][:, 8] >= 0).all()   # shared expert never capped
+
+
+def test_fine_grained_routing_override():
+    T, E = 50, 256
+    # GELU experts: the oracle's forward_given_routing evaluates the GELU layer on a given routing
+    w = synthetic.make("dsv3_decode", T=T, d=256, f=256, seed=8, activation="gelu")
+    rng = np.random.default_rng(8)
+    idx = np.stack([rng.choice(E, size=8, replace=False) for _ in range(T)]).astype(np.int32)
+    gate = rng.uniform(0.01, 0.3, size=(T, 8)).astype(np.float32)
+    got, dbg = run_layer(w, torch, route_idx=idx, route_gate=gate)
+    np.testing.assert_array_equal(dbg["idx"][:, :8], idx)
+    assert (dbg["idx"][:, 8] == E).all() and (dbg["gate"][:, 8] == 1.0).all()
+    full_idx = np.concatenate([idx, np.full((T, 1), E, np.int32)], axis=1)
+    full_gate = np.concatenate([gate.astype(np.float64), np.ones((T, 1))], axis=1)
+    ref = oracle.forward_given_routing(w.x, w.w_gate, w.w_up, w.w_down, full_idx, full_gate)
+    assert normwise_err(got, ref) <= TOL["bf16"]
+
+
+def test_dsv3_decode_full():
+    # DeepSeek-V3 shapes: d=7168, 256 routed experts of width 2048, top-8, one shared expert, 8 tokens
+    w = synthetic.make("dsv3_decode")
+    _check(w, label="dsv3 decode full")
+    del w
+    gc.collect()
+
+
+def test_dsv3_prefill_full_sampled():
+    w = synthetic.make("dsv3_prefill")
+    print(f"[variants] dsv3 prefill full: T={w.T}", flush=True)
+    got, dbg = run_layer(w, torch)
+    ref_all = _oracle(w, tokens=[0])
+    np.testing.assert_array_equal(dbg["idx"], ref_all["idx"])
+    c, o, p, pos = oracle.permute_cap(dbg["idx"], w.E + w.n_shared, -1)
+    np.testing.assert_array_equal(dbg["counts"], c)
+    np.testing.assert_array_equal(dbg["pos"], pos)
+    cand = _sample(dbg, w.E + w.n_shared, w.T, 6, seed=2)
+    toks = sorted(np.random.default_rng(3).choice(cand, size=min(40, len(cand)), replace=False).tolist())
+    ref = _oracle(w, tokens=toks)
+    err = normwise_err(got[toks], ref["out"])
+    print(f"[variants] dsv3 prefill full: {len(toks)} tokens, normwise error {err:.3e}", flush=True)
     assert err <= TOL["bf16"]
     del w
     gc.collect()
