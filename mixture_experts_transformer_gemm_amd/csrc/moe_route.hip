@@ -406,18 +406,37 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = (cap >= 0 && e < E_cap && (int64_t)s_cnt[e] > cap) ? (int)cap : s_cnt[e];
-      offsets[e] = acc;
-      counts[e] = c;
-      s_off[e] = acc;
-      s_lim[e] = c;
-      s_base[e] = 0;
-      acc += c;
+  if (wave == 0) {
+    // exclusive scan of the capped counts: lane l owns experts kPer*l .. kPer*l + kPer - 1
+    constexpr int kPer = (kPermMaxE + 63) / 64;
+    int c[kPer], local = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = lane * kPer + j;
+      c[j] = 0;
+      if (e < E) c[j] = (cap >= 0 && e < E_cap && (int64_t)s_cnt[e] > cap) ? (int)cap : s_cnt[e];
+      local += c[j];
     }
-    offsets[E] = acc;
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    int acc = incl - local;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = lane * kPer + j;
+      if (e < E) {
+        offsets[e] = acc;
+        counts[e] = c[j];
+        s_off[e] = acc;
+        s_lim[e] = c[j];
+        s_base[e] = 0;
+      }
+      acc += c[j];
+    }
+    if (lane == 63) offsets[E] = incl;
   }
   __syncthreads();
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -433,16 +452,53 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
         my_e[s] = (e >= 0 && e < E) ? e : -1;
       }
     }
-    for (int e = 0; e < E; ++e) {
+    // ranks inside the wavefront: expert by expert over all E when the
+    // wavefront holds at least E assignments, else only over the experts
+    // present in it (the lowest unranked slot of the first lane that has one
+    // names the next), which is at most as many iterations as assignments
+    uint32_t pending = 0;
+#pragma unroll
+    for (int s = 0; s < kPermMaxK; ++s)
+      if (my_e[s] >= 0) pending |= 1u << s;
+    int n_assign = __popc(pending);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) n_assign += __shfl_xor(n_assign, off, 64);
+    if (n_assign >= E) {
+      for (int e = 0; e < E; ++e) {
+        bool sel = false;
+#pragma unroll
+        for (int s = 0; s < kPermMaxK; ++s) sel = sel || (my_e[s] == e);
+        const uint64_t m = __ballot(sel);
+        if (lane == 0) s_wave[wave][e] = __popcll(m);
+        const int r = __popcll(m & lt_mask);
+#pragma unroll
+        for (int s = 0; s < kPermMaxK; ++s)
+          if (my_e[s] == e) my_rank[s] = r;
+      }
+      pending = 0;
+    } else {
+      for (int e = lane; e < E; e += 64) s_wave[wave][e] = 0;
+    }
+    while (true) {  // exits together: `have` is the same in every lane
+      int cand = -1;
+#pragma unroll
+      for (int s = kPermMaxK - 1; s >= 0; --s)
+        if ((pending >> s) & 1u) cand = my_e[s];
+      const uint64_t have = __ballot(cand >= 0);
+      if (have == 0) break;
+      const int e = __shfl(cand, __ffsll((unsigned long long)have) - 1, 64);
       bool sel = false;
 #pragma unroll
       for (int s = 0; s < kPermMaxK; ++s) sel = sel || (my_e[s] == e);
       const uint64_t m = __ballot(sel);
-      if (lane == 0) s_wave[wave][e] = __popcll(m);
       const int r = __popcll(m & lt_mask);
 #pragma unroll
       for (int s = 0; s < kPermMaxK; ++s)
-        if (my_e[s] == e) my_rank[s] = r;
+        if (my_e[s] == e) {
+          my_rank[s] = r;
+          pending &= ~(1u << s);
+        }
+      if (lane == 0) s_wave[wave][e] = __popcll(m);
     }
     __syncthreads();
     if (t < T) {
