@@ -67,9 +67,12 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
     p.splits = s;
   } else {
     p.path = PATH_TILED;
-    // about K*T/Et rows per expert: the tile height that wastes little of it
+    // about K*T/Et rows per expert. Taller tiles reuse each weight tile over
+    // more rows and run the 8-wavefront kernel; measured on the Grok-1 and
+    // 256-expert shapes, 256-row tiles win from about 100 rows per expert
+    // on even when half of an expert's last tile is empty
     const int64_t r = p.rows_cap / Et;
-    p.bm = r <= 96 ? 64 : (r <= 384 ? 128 : 256);
+    p.bm = r <= 32 ? 64 : (r <= 96 ? 128 : 256);
     // 8-bit weights: one row tile per expert up to 128 rows, so each weight
     // tile is streamed from HBM once
     if (wdt == GROK_MOE_I8 && r <= 384) p.bm = 128;
