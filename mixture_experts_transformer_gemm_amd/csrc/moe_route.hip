@@ -156,8 +156,9 @@ hipError_t launch_router(int act_f32, const void* x, const void* router_w, int64
 // Fine-grained layers route over hundreds of experts (256 in DeepSeek-V3,
 // book ch. 10, section 10.1 table). The logits become a [T][E] GEMM in two
 // kernels: router_gemm_kernel forms split-K partial logits in fp64 (each
-// bf16 product is exact in fp64), router_topk_wave_kernel sums the partials
-// in split order and runs softmax and top-k with one wavefront per token.
+// bf16 product is exact in fp64), router_topk_block_kernel sums the
+// partials in split order and runs softmax and top-k with one workgroup per
+// token.
 
 // Workgroup tile: 64 tokens x 64 experts, reduction chunks of 64 staged as
 // bf16 in LDS (rows padded to 72 values, so the 16 rows that a wavefront
@@ -235,40 +236,37 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const bf16_bits* __res
   }
 }
 
-// One wavefront per token; lane l holds experts l, l + 64, l + 128, l + 192.
-__global__ __launch_bounds__(256) void router_topk_wave_kernel(const double* __restrict__ P, int S, int64_t T, int E,
-                                                               int k, int ns, int renorm,
-                                                               const float* __restrict__ bias,
-                                                               int32_t* __restrict__ idx, float* __restrict__ gate) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// One workgroup per token, thread e holding expert e (E <= 256): the split
+// partials of its logit summed in split order, softmax with workgroup
+// reductions in fixed order, then k rounds of arg-max over (p + b, index).
+__global__ __launch_bounds__(256) void router_topk_block_kernel(const double* __restrict__ P, int S, int64_t T, int E,
+                                                                int k, int ns, int renorm,
+                                                                const float* __restrict__ bias,
+                                                                int32_t* __restrict__ idx, float* __restrict__ gate) {
+  __shared__ double s_red[4];
+  __shared__ double s_key[4], s_p[4];
+  __shared__ int s_idx[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = k + ns;
-  for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t < T; t += (int64_t)gridDim.x * 4) {
-    double lg[4], p[4], key[4];
-    bool live[4], taken[4];
-    double mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      live[j] = e < E;
-      taken[j] = false;
-      lg[j] = 0.0;
-      if (live[j])
-        for (int s = 0; s < S; ++s) lg[j] += P[((int64_t)s * T + t) * E + e];
-      if (live[j]) mx = fmax(mx, lg[j]);
-    }
-    mx = wave_max_f64(mx);
-    double zs = 0.0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p[j] = live[j] ? exp(lg[j] - mx) : 0.0;
-      zs += p[j];
-    }
-    const double z = wave_sum_f64(zs);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p[j] = p[j] / z;
-      key[j] = live[j] ? p[j] + (bias ? (double)bias[lane + 64 * j] : 0.0) : -INFINITY;
-    }
+  const bool live = tid < E;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    double lg = 0.0;
+    if (live)
+      for (int s = 0; s < S; ++s) lg += P[((int64_t)s * T + t) * E + tid];
+    double m = wave_max_f64(live ? lg : -INFINITY);
+    if (lane == 0) s_red[wave] = m;
+    __syncthreads();
+    m = fmax(fmax(s_red[0], s_red[1]), fmax(s_red[2], s_red[3]));
+    __syncthreads();
+    const double ex = live ? exp(lg - m) : 0.0;
+    double z = wave_sum_f64(ex);
+    if (lane == 0) s_red[wave] = z;
+    __syncthreads();
+    z = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+    __syncthreads();
+    const double p = ex / z;
+    const double key = live ? p + (bias ? (double)bias[tid] : 0.0) : -INFINITY;
+    bool taken = false;
     double gsel[8];
     int isel[8];
 #pragma unroll
@@ -276,18 +274,8 @@ __global__ __launch_bounds__(256) void router_topk_wave_kernel(const double* __r
       gsel[s] = 0.0;
       isel[s] = 0;
       if (s < k) {
-        // this lane's best untaken expert, then the wavefront's; key (p + bias desc, index asc)
-        double kv = -INFINITY, pv = 0.0;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = lane + 64 * j;
-          if (live[j] && !taken[j] && (key[j] > kv || (key[j] == kv && e < bi))) {
-            kv = key[j];
-            pv = p[j];
-            bi = e;
-          }
-        }
+        double kv = (live && !taken) ? key : -INFINITY, pv = p;
+        int bi = tid;
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
           const double ko = __shfl_xor(kv, off, 64);
@@ -299,14 +287,29 @@ __global__ __launch_bounds__(256) void router_topk_wave_kernel(const double* __r
             bi = io;
           }
         }
+        if (lane == 0) {
+          s_key[wave] = kv;
+          s_p[wave] = pv;
+          s_idx[wave] = bi;
+        }
+        __syncthreads();
+        kv = s_key[0];
+        pv = s_p[0];
+        bi = s_idx[0];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (lane + 64 * j == bi) taken[j] = true;
+        for (int w = 1; w < 4; ++w)
+          if (s_key[w] > kv || (s_key[w] == kv && s_idx[w] < bi)) {
+            kv = s_key[w];
+            pv = s_p[w];
+            bi = s_idx[w];
+          }
+        __syncthreads();
+        if (tid == bi) taken = true;
         gsel[s] = pv;
         isel[s] = bi;
       }
     }
-    if (lane == 0) {
+    if (tid == 0) {
       double sum = 0.0;
 #pragma unroll
       for (int s = 0; s < 8; ++s) sum += gsel[s];
@@ -331,10 +334,9 @@ hipError_t launch_router_many(const bf16_bits* x, const bf16_bits* router_w, int
   hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(256), 0, stream, x, router_w, T, d, E, P);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  int64_t blocks = (T + 3) / 4;
-  if (blocks > 16384) blocks = 16384;
+  int64_t blocks = T < 16384 ? T : 16384;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(router_topk_wave_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, P, splits, T, E, k, ns,
+  hipLaunchKernelGGL(router_topk_block_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, P, splits, T, E, k, ns,
                      renorm, bias, idx, gate);
   return hipGetLastError();
 }
