@@ -251,8 +251,20 @@ __global__ __launch_bounds__(256) void router_topk_block_kernel(const double* __
   const bool live = tid < E;
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
     double lg = 0.0;
-    if (live)
-      for (int s = 0; s < S; ++s) lg += P[((int64_t)s * T + t) * E + tid];
+    if (live) {
+      // eight partials loaded at a time, added in split order
+      const double* pe = P + t * E + tid;
+      const int64_t stride = T * E;
+      int s = 0;
+      for (; s + 8 <= S; s += 8) {
+        double v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = pe[(int64_t)(s + q) * stride];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) lg += v[q];
+      }
+      for (; s < S; ++s) lg += pe[(int64_t)s * stride];
+    }
     double m = wave_max_f64(live ? lg : -INFINITY);
     if (lane == 0) s_red[wave] = m;
     __syncthreads();
@@ -488,7 +500,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
         if ((pending >> s) & 1u) cand = my_e[s];
       const uint64_t have = __ballot(cand >= 0);
       if (have == 0) break;
-      const int e = __shfl(cand, __ffsll((unsigned long long)have) - 1, 64);
+      const int e = __builtin_amdgcn_readlane(cand, __ffsll((unsigned long long)have) - 1);
       bool sel = false;
 #pragma unroll
       for (int s = 0; s < kPermMaxK; ++s) sel = sel || (my_e[s] == e);
