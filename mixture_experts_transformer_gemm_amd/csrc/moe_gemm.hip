@@ -1,8 +1,8 @@
 // fp32 grouped expert GEMMs of the Grok-1 MoE layer for gfx950 (MI355X).
 //
 // Expert e is a gated FFN (Grok-1 field guide, "MoE 子层"; Grok-1 book ch. 10,
-// section 10.4): two input projections, GELU on the gate branch, elementwise
-// product, and a down projection. Rows are the expert-contiguous permutation
+// section 10.4): two input projections, GELU (SiLU for SwiGLU experts) on
+// the gate branch, elementwise product, and a down projection. Rows are the expert-contiguous permutation
 // of the tokens, so each expert is one segment of a grouped GEMM (book
 // ch. 11, section 11.3.1: sparse reorder + grouped GEMM). Used for fp32
 // activations and weights, where there is no bf16 MFMA to feed: plain fp32

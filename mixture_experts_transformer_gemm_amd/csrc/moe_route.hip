@@ -1,11 +1,13 @@
-// Router (logits -> softmax -> top-k), token permutation and gate-weighted
-// combine of the Grok-1 MoE layer, for gfx950.
+// Router (logits -> softmax -> top-k), token permutation, gate-weighted
+// combine and the sandwich RMSNorms of the MoE layer, for gfx950.
 //
 // Routing follows the Grok-1 code shown in the Grok-1 book ch. 10, section
 // 10.3.1: softmax over all experts first, then top-k, and the gates are the
-// selected probabilities with no renormalisation. The logits are accumulated
-// in fp64 (every bf16*bf16 or fp32*fp32 product is exact in fp64), so the
-// expert choice only depends on the summation order at the 1e-13 level.
+// selected probabilities with no renormalisation (renormalised on request,
+// as Mixtral does; a per-expert bias can steer the choice, as in
+// DeepSeek-V3's routing). The logits are accumulated in fp64 (every
+// bf16*bf16 or fp32*fp32 product is exact in fp64), so the expert choice
+// only depends on the summation order at the 1e-13 level.
 #include "moe_internal.h"
 
 namespace gmoe {

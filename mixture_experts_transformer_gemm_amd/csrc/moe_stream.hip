@@ -29,7 +29,7 @@
 // Gate/up pass: a wavefront owns 8 gate channels and the same 8 up channels
 // (16 weight rows, one 16x16x32 MFMA tile per 16 activation rows); lanes
 // holding gate results take the matching up results from lane + 32 and form
-// GELU(gate) * up. Down pass: a wavefront owns 16 output channels, split over
+// act(gate) * up (GELU, or SiLU for SwiGLU experts). Down pass: a wavefront owns 16 output channels, split over
 // the reduction into `gridDim.y` partial sums (fixed order, reduced by the
 // combine stage).
 //

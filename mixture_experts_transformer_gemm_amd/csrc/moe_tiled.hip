@@ -7,29 +7,28 @@
 // "MoE 子层": two input projections, GELU on one, elementwise product).
 // Down pass: Y = H Wd^T -> fp32.
 //
-// Workgroup tile: BM rows x 256 weight rows, 4 wavefronts. For the gate/up
-// pass the 256 weight rows are 128 gate channels and the same 128 up
-// channels, so GELU(gate) * up is formed in registers. Products use
-// v_mfma_f32_32x32x16_bf16 with the weight fragment as the "A" operand (32
-// channels) and the activation fragment as "B" (32 rows): lane l supplies row
-// (l mod 32) and the 8 reduction values of group l / 32; result register v of
-// lane l is C[8 (v / 4) + 4 (l / 32) + (v mod 4)][l mod 32], so each lane
-// owns runs of 4 consecutive channels of one row.
+// Workgroup tile: BM rows x 256 weight rows (BM = 64 or 128 with 4
+// wavefronts, 256 with 8). For the gate/up pass the 256 weight rows are 128
+// gate channels and the same 128 up channels, so act(gate) * up is formed in
+// registers. Products use v_mfma_f32_32x32x16_bf16 with the weight fragment
+// as the "A" operand (32 channels) and the activation fragment as "B" (32
+// rows): lane l supplies row (l mod 32) and the 8 reduction values of group
+// l / 32; result register v of lane l is C[8 (v / 4) + 4 (l / 32) + (v mod
+// 4)][l mod 32], so each lane owns runs of 4 consecutive channels of one row.
 //
-// Two feeds of LDS:
-//  * bf16 weights (dma_kernel): global_load_lds_dwordx4 writes each stage of
-//    32 reduction values straight into LDS (lane i of a wavefront lands at
-//    LDS base + 16 i), four LDS stages, loads issued three stages ahead, an
-//    explicit vmcnt wait and one barrier per stage. No staging registers.
-//  * 8-bit weights (staged_kernel): 64-wide stages pass through registers so
-//    the int8 values can be widened to bf16 (exact) on the way into LDS; two
-//    LDS stages, loads issued a stage ahead of their LDS write.
+// Both operands reach LDS by global_load_lds_dwordx4 (no staging registers):
+// stages of 64 reduction values, as many stages as fit in 144 KB (2 for the
+// 256-row tile), loads issued NS - 1 stages ahead, one vmcnt wait and one
+// barrier per stage. 8-bit weights stay int8 in LDS and are widened to bf16
+// after the fragment read (exact); their per-channel scales are applied in
+// the epilogue. The down pass can split its reduction over grid y (partial
+// sums in Y, added in the combine).
 //
 // Tile order: the tiles that exist (sum over experts of ceil(rows / BM),
 // times the channel tiles) are split into 8 contiguous ranges, one per XCD
-// (workgroup i runs on XCD i mod 8); each range walks groups of 8 row tiles
-// with the row tile fastest, so the workgroups resident on one XCD share
-// weight tiles through its L2.
+// (workgroup i runs on XCD i mod 8); each range walks groups of kGroupM row
+// tiles with the row tile fastest, so the workgroups resident on one XCD
+// share weight tiles through its L2.
 #include "moe_device.h"
 
 #include <type_traits>
