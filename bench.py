@@ -206,10 +206,15 @@ def main():
     ms_per_step = elapsed / args.steps * 1e3
     tokens_per_s = w.T * args.steps / elapsed
     stage_ms = {n: 0.0 for n in gm.STAGES}
+    step_ms = []
     for s in range(args.steps):
         for i, n in enumerate(gm.STAGES):
             stage_ms[n] += ev.elapsed_ms(6 * s + i, 6 * s + i + 1) / args.steps
+        step_ms.append(ev.elapsed_ms(6 * s, 6 * s + 5))
     ev.close()
+    # per-step device time (first stage event to last) over the timed steps
+    q = np.percentile(np.array(step_ms), [10, 50, 90])
+    step_dist = {"p10": round(float(q[0]), 5), "median": round(float(q[1]), 5), "p90": round(float(q[2]), 5)}
     log("stage ms: " + ", ".join(f"{n}={v:.4f}" for n, v in stage_ms.items()))
 
     # algorithmic work of the dominant kernel (gate/up grouped GEMM + GELU*up):
@@ -264,7 +269,8 @@ def main():
         "cpu_baseline": cpu,
         "layer": {"ms": round(ms_per_step, 5), "GBps": round(layer_bytes / (ms_per_step / 1e3) / 1e9, 1),
                   "TFLOPs": round(layer_flops / (ms_per_step / 1e3) / 1e12, 2),
-                  "stage_ms": {k2: round(v, 5) for k2, v in stage_ms.items()}},
+                  "stage_ms": {k2: round(v, 5) for k2, v in stage_ms.items()},
+                  "device_step_ms": step_dist},
     }
     print(json.dumps(result), flush=True)
 
