@@ -293,7 +293,16 @@ def cpu_baseline(w, name, args):
                      norm_eps=w.norm_eps, n_shared=w.n_shared, router_bias=w.router_bias, nthreads=cores)
         passes += 1
         dt = time.perf_counter() - t0
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(n * passes / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": f"first {n} of the {w.T} tokens as their own batch, {passes} pass(es), whole layer "
                       f"(routing, {w.k} experts per token, combine) in fp64: {dt:.2f} s"}
 

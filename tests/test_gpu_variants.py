@@ -265,3 +265,35 @@ def test_dsv3_prefill_full_sampled():
     assert err <= TOL["bf16"]
     del w
     gc.collect()
+
+
+def _full_sampled(w, label, n_random=6, max_tokens=40):
+    print(f"[variants] {label}: T={w.T}", flush=True)
+    got, dbg = run_layer(w, torch)
+    ref_all = _oracle(w, tokens=[0])
+    np.testing.assert_array_equal(dbg["idx"], ref_all["idx"])
+    np.testing.assert_array_equal(dbg["pos"], ref_all["pos"])
+    if w.norm_pre is not None:
+        np.testing.assert_array_equal(dbg["u"], ref_all["u"])
+    cand = _sample(dbg, w.E + w.n_shared, w.T, n_random, seed=4)
+    toks = sorted(np.random.default_rng(5).choice(cand, size=min(max_tokens, len(cand)), replace=False).tolist())
+    ref = _oracle(w, tokens=toks)
+    err = normwise_err(got[toks], ref["out"])
+    print(f"[variants] {label}: {len(toks)} tokens, normwise error {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+
+
+def test_mixtral_prefill_full_sampled():
+    # Mixtral 8x22B shapes at 8192 tokens: the tiled path with SiLU and renormalised gates
+    w = synthetic.make("mixtral_prefill")
+    _full_sampled(w, "mixtral prefill full")
+    del w
+    gc.collect()
+
+
+def test_sandwich_prefill_full_sampled():
+    # the sandwich sub-layer at the Grok-1 prefill shape (pre-norm output checked bitwise for all tokens)
+    w = synthetic.make("prefill", sandwich=True)
+    _full_sampled(w, "sandwich prefill full")
+    del w
+    gc.collect()
