@@ -355,7 +355,8 @@ hipError_t launch_router_many(const bf16_bits* x, const bf16_bits* router_w, int
   return hipGetLastError();
 }
 
-// Caller-given routing [T][k] plus the ns shared slots -> [T][k + ns].
+// Caller-given routing [T][k] plus the ns shared slots -> [T][k + ns]. A
+// caller index outside [0, E) becomes -1 (dropped by the permutation).
 __global__ __launch_bounds__(256) void append_shared_kernel(const int32_t* __restrict__ ridx,
                                                             const float* __restrict__ rgate, int64_t T, int E, int k,
                                                             int ns, int32_t* __restrict__ idx,
@@ -364,7 +365,12 @@ __global__ __launch_bounds__(256) void append_shared_kernel(const int32_t* __res
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < T * K; i += (int64_t)gridDim.x * 256) {
     const int64_t t = i / K;
     const int s = (int)(i - t * K);
-    idx[i] = s < k ? ridx[t * k + s] : E + (s - k);
+    int e = E + (s - k);
+    if (s < k) {
+      e = ridx[t * k + s];
+      if (e < 0 || e >= E) e = -1;  // outside the routed experts: dropped, never a shared expert
+    }
+    idx[i] = e;
     gate[i] = s < k ? rgate[t * k + s] : 1.0f;
   }
 }

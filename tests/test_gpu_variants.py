@@ -231,11 +231,17 @@ def test_fine_grained_routing_override():
     rng = np.random.default_rng(8)
     idx = np.stack([rng.choice(E, size=8, replace=False) for _ in range(T)]).astype(np.int32)
     gate = rng.uniform(0.01, 0.3, size=(T, 8)).astype(np.float32)
+    idx[3, 2] = E          # the shared expert's index is not a routed expert: dropped
+    idx[7, 0] = -5         # out of range: dropped
     got, dbg = run_layer(w, torch, route_idx=idx, route_gate=gate)
-    np.testing.assert_array_equal(dbg["idx"][:, :8], idx)
+    dropped = (idx < 0) | (idx >= E)
+    np.testing.assert_array_equal(dbg["idx"][:, :8], np.where(dropped, -1, idx))
+    assert (dbg["pos"][:, :8][dropped] == -1).all() and (dbg["pos"][:, :8][~dropped] >= 0).all()
     assert (dbg["idx"][:, 8] == E).all() and (dbg["gate"][:, 8] == 1.0).all()
-    full_idx = np.concatenate([idx, np.full((T, 1), E, np.int32)], axis=1)
-    full_gate = np.concatenate([gate.astype(np.float64), np.ones((T, 1))], axis=1)
+    ref_idx = np.where(dropped, 0, idx)                # any valid expert, with gate 0
+    ref_gate = np.where(dropped, 0.0, gate.astype(np.float64))
+    full_idx = np.concatenate([ref_idx, np.full((T, 1), E, np.int32)], axis=1)
+    full_gate = np.concatenate([ref_gate, np.ones((T, 1))], axis=1)
     ref = oracle.forward_given_routing(w.x, w.w_gate, w.w_up, w.w_down, full_idx, full_gate)
     assert normwise_err(got, ref) <= TOL["bf16"]
 
