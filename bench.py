@@ -264,7 +264,8 @@ def main():
         "config": {"workload": workload, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k,
                    "weights": w.w_dtype, "experts_hit": n_hit, "activation": w.activation,
                    "renormalize": w.renormalize, "capacity_factor": w.capacity_factor, "sandwich": args.sandwich,
-                   "n_shared": w.n_shared, "router_bias": w.router_bias is not None, "rows_run": rows},
+                   "n_shared": w.n_shared, "router_bias": w.router_bias is not None, "rows_run": rows,
+                   "rows_per_expert": counts.tolist() if len(counts) <= 16 else None},
         "roofline": roof,
         "cpu_baseline": cpu,
         "layer": {"ms": round(ms_per_step, 5), "GBps": round(layer_bytes / (ms_per_step / 1e3) / 1e9, 1),

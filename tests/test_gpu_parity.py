@@ -39,7 +39,7 @@ def _full_check(w, scales=None, expect_exact_routing=True):
     return got, dbg, err
 
 
-@pytest.mark.parametrize("T", [1, 5, 8, 16, 37, 64, 100, 128, 129, 300, 777])
+@pytest.mark.parametrize("T", [1, 5, 8, 16, 37, 63, 64, 65, 100, 128, 129, 257, 300, 777, 2049])
 def test_bf16_layer_small(T):
     w = synthetic.make("decode", T=T, d=256, f=512, seed=T)
     _full_check(w)
@@ -173,3 +173,17 @@ def test_binding_errors_raise():
     with pytest.raises(gm.GrokMoeError) as ei:
         gm.grok_moe_forward_ex(dev["x"], dev["router_w"], dev["w_gate"], dev["w_up"], dev["w_down"], workspace=ws)
     assert ei.value.code == gm.EWORKSPACE
+
+
+@pytest.mark.parametrize("T", [40, 2049])
+def test_router_sends_every_token_to_two_experts(T):
+    # a constant feature with router weights +100 (expert 0) and +50 (expert 5): every token picks
+    # (0, 5), so two segments hold all T rows and six experts are empty (bf16-exact inputs)
+    w = synthetic.make("decode", T=T, d=256, f=512, seed=14)
+    w.x[:, w.d - 1] = synthetic.f32_to_bf16_bits(np.array([1.0], np.float32))[0]
+    bias = np.zeros(w.E, np.float32)
+    bias[0], bias[5] = 100.0, 50.0
+    w.router_w[:, w.d - 1] = synthetic.f32_to_bf16_bits(bias)
+    got, dbg, _ = _full_check(w)
+    assert (dbg["idx"] == [0, 5]).all()
+    assert list(dbg["counts"]) == [T, 0, 0, 0, 0, T, 0, 0]
