@@ -16,7 +16,9 @@
 // at compute time; here one fp32 scale per output channel, applied in the
 // epilogue).
 //
-// Workgroup = 8 wavefronts, each streaming its own 16 weight rows. The
+// Workgroup = 8 wavefronts, each streaming its own 16 weight rows (32 for
+// 8-bit weights in chunks of more than 32 rows, where the activation
+// fragment reads bound the stage: each fragment then feeds two MFMAs). The
 // segment's activation rows (token rows of x through the permutation, or H
 // rows) of each stage are loaded once per workgroup, spread over the
 // wavefronts for as many load instructions as the rows need, and shared by
@@ -61,13 +63,15 @@ __device__ __forceinline__ void dma16s(const void* src, char* lds_base) { dma16_
 // Segments processed in chunks of up to 16*MT rows (MT = 1, 2, 4, 8; chunk
 // z of a segment along grid z). W8: 8-bit weights.
 constexpr int kBW = 8;               // wavefronts per workgroup
-constexpr int kBWRows = 16 * kBW;    // weight rows per workgroup stage
 
 // A stage holds kRowB bytes of every weight row: 64 reduction values of bf16
 // weights, 128 of 8-bit weights; activation rows (bf16) hold the same
 // reduction values: 128 or 256 bytes.
-template <int MT, bool W8>
+// WT: 16-row weight tiles per wavefront (each activation fragment read from
+// LDS then feeds WT MFMAs).
+template <int MT, bool W8, int WT = 1>
 struct BsCfg {
+  static constexpr int kBWRows = 16 * WT * kBW;          // weight rows per workgroup stage
   static constexpr int XR = 16 * MT;                     // activation rows per chunk
   static constexpr int KS = W8 ? 128 : 64;               // reduction values per stage
   static constexpr int AROWB = KS * 2;                   // activation bytes per row and stage
@@ -100,17 +104,18 @@ __device__ __forceinline__ void wait_stages(int p) {
   __asm__ __volatile__("" ::: "memory");  // no LDS access moves above the wait
 }
 
-template <bool GATEUP, int MT, bool W8>
+template <bool GATEUP, int MT, bool W8, int WT>
 __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __restrict__ A, RouteView rv,
                                                           const void* __restrict__ w0, const void* __restrict__ w1,
                                                           const float* __restrict__ scales, int64_t T, int K,
                                                           int N, int E, int64_t rows_cap, int act,
                                                           void* __restrict__ out) {
-  using C = BsCfg<MT, W8>;
+  using C = BsCfg<MT, W8, WT>;
+  constexpr int kBWRows = C::kBWRows;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int kChW = GATEUP ? 8 : 16;  // output channels per wavefront
+  constexpr int kChW = (GATEUP ? 8 : 16) * WT;  // output channels per wavefront
   const int nblk = N / (kBW * kChW);
   const int e = blockIdx.x / nblk;
   const int nb = blockIdx.x - e * nblk;
@@ -127,17 +132,19 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
   const int mv = (rows + 15) >> 4;                // 16-row MFMA tiles with rows
   constexpr size_t wsz = W8 ? 1 : 2;
 
-  // this lane's sources: two weight instructions (rows 8q + lane / 8 of the
-  // wavefront's 16) and the activation instructions wave, wave + 8, ... < na
-  const char* wsrc[2];
+  // this lane's sources: 2 WT weight instructions (rows 8q + lane / 8 of the
+  // wavefront's 16 WT; gate/up: tile w holds gate channels 8w.. in rows
+  // 16w..16w+7 and the same up channels in rows 16w+8..16w+15) and the
+  // activation instructions wave, wave + 8, ... < na
+  const char* wsrc[2 * WT];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < 2 * WT; ++q) {
     const int r = 8 * q + (lane >> 3);
-    const int R = 16 * wave + r;  // ring row
+    const int R = 16 * WT * wave + r;  // ring row
     const int c = rslot(R, lane & 7);
     const char* row;
     if (GATEUP)
-      row = (const char*)(r < 8 ? w0 : w1) + ((int64_t)e * N + c0 + (r & 7)) * K * wsz;
+      row = (const char*)((r & 8) == 0 ? w0 : w1) + ((int64_t)e * N + c0 + 8 * (r >> 4) + (r & 7)) * K * wsz;
     else
       row = (const char*)w0 + ((int64_t)e * N + c0 + r) * K * wsz;
     wsrc[q] = row + kbeg * wsz + c * 16;
@@ -167,12 +174,14 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
   const int rot = (int)(((unsigned)blockIdx.x * 37u + (unsigned)sp * 11u + (unsigned)blockIdx.z * 5u) % (unsigned)nk);
 
   const int r16 = lane & 15, g = lane >> 4;
-  f32x4 acc[MT];
+  f32x4 acc[WT][MT];
 #pragma unroll
-  for (int j = 0; j < MT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int w = 0; w < WT; ++w)
+#pragma unroll
+    for (int j = 0; j < MT; ++j) acc[w][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // MFMA step on tiles 0..MV-1: weight fragment wa, activation chunk cx
-  auto tiles = [&](const char* b, u32x4 wa, int cx, auto mv_tag) __attribute__((always_inline)) {
+  // MFMA step on tiles 0..MV-1: weight fragments wa[WT], activation chunk cx
+  auto tiles = [&](const char* b, const u32x4* wa, int cx, auto mv_tag) __attribute__((always_inline)) {
     constexpr int MV = decltype(mv_tag)::value;
     u32x4 xa[MV];
 #pragma unroll
@@ -182,19 +191,21 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
       xa[j] = *reinterpret_cast<const u32x4*>(b + C::kActOff + xr * C::AROWB + slot * 16);
     }
 #pragma unroll
-    for (int j = 0; j < MV; ++j) acc[j] = mfma16(wa, xa[j], acc[j]);
+    for (int w = 0; w < WT; ++w)
+#pragma unroll
+      for (int j = 0; j < MV; ++j) acc[w][j] = mfma16(wa[w], xa[j], acc[w][j]);
   };
 
   auto run = [&](auto naw_tag, auto mv_tag) __attribute__((always_inline)) {
     constexpr int NAW = decltype(naw_tag)::value;
-    constexpr int Q = 2 + NAW;  // this wavefront's load instructions per stage
+    constexpr int Q = 2 * WT + NAW;  // this wavefront's load instructions per stage
     constexpr int NS = C::NS;
     auto issue = [&](int stage, int slot) __attribute__((always_inline)) {
       int ks = stage + rot;
       if (ks >= nk) ks -= nk;
       char* dst = lds + slot * C::kStageB;
-      dma16s(wsrc[0] + (size_t)ks * kRowB, dst + (16 * wave) * kRowB);
-      dma16s(wsrc[1] + (size_t)ks * kRowB, dst + (16 * wave + 8) * kRowB);
+#pragma unroll
+      for (int q = 0; q < 2 * WT; ++q) dma16s(wsrc[q] + (size_t)ks * kRowB, dst + (16 * WT * wave + 8 * q) * kRowB);
 #pragma unroll
       for (int a = 0; a < NAW; ++a)
         dma16s(asrc[a] + (size_t)ks * C::AROWB, dst + C::kActOff + (wave + kBW * a) * 1024);
@@ -210,12 +221,16 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
       lds_barrier();
       if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
       const char* b = lds + (kt % NS) * C::kStageB;
-      const int wr = 16 * wave + r16;
       if (!W8) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           const int c = 4 * s + g;  // reduction values [32s + 8g, +8)
-          const u32x4 wa = *reinterpret_cast<const u32x4*>(b + wr * kRowB + rslot(wr, c) * 16);
+          u32x4 wa[WT];
+#pragma unroll
+          for (int w = 0; w < WT; ++w) {
+            const int wr = 16 * WT * wave + 16 * w + r16;
+            wa[w] = *reinterpret_cast<const u32x4*>(b + wr * kRowB + rslot(wr, c) * 16);
+          }
           tiles(b, wa, c, mv_tag);
         }
       } else {
@@ -225,9 +240,13 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int c = 4 * h + g;
-          const u32x4 q = *reinterpret_cast<const u32x4*>(b + wr * kRowB + rslot(wr, c) * 16);
-          u32x4 lo, hi;
-          i8x16_to_frags(q, lo, hi);
+          u32x4 lo[WT], hi[WT];
+#pragma unroll
+          for (int w = 0; w < WT; ++w) {
+            const int wr = 16 * WT * wave + 16 * w + r16;
+            const u32x4 q = *reinterpret_cast<const u32x4*>(b + wr * kRowB + rslot(wr, c) * 16);
+            i8x16_to_frags(q, lo[w], hi[w]);
+          }
           tiles(b, lo, 8 * h + 2 * g, mv_tag);
           tiles(b, hi, 8 * h + 2 * g + 1, mv_tag);
         }
@@ -259,87 +278,104 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
     run_naw(std::integral_constant<int, 0>{});
 
 #pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    if (j < mv) {
-      const int m = 16 * j + r16;  // activation row (within the chunk) of this lane's results
-      if (GATEUP) {
-        // lanes with g < 2 hold gate channels 4g..4g+3, lane + 32 the same up channels
-        float up[4];
+  for (int w = 0; w < WT; ++w) {
+    // weight tile w: gate/up channels cw..cw+7, or down channels cw..cw+15
+    const int cw = c0 + (GATEUP ? 8 : 16) * w;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) up[v] = __shfl(acc[j][v], lane + 32, 64);
-        if (g < 2 && m < rows) {
-          float h[4];
+    for (int j = 0; j < MT; ++j) {
+      if (j < mv) {
+        const int m = 16 * j + r16;  // activation row (within the chunk) of this lane's results
+        if (GATEUP) {
+          // lanes with g < 2 hold gate channels 4g..4g+3, lane + 32 the same up channels
+          float up[4];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float gt = acc[j][v], u = up[v];
-            if (W8) {
-              gt *= scales[(int64_t)e * N + c0 + 4 * g + v];
-              u *= scales[(int64_t)E * N + (int64_t)e * N + c0 + 4 * g + v];
+          for (int v = 0; v < 4; ++v) up[v] = __shfl(acc[w][j][v], lane + 32, 64);
+          if (g < 2 && m < rows) {
+            float h[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              float gt = acc[w][j][v], u = up[v];
+              if (W8) {
+                gt *= scales[(int64_t)e * N + cw + 4 * g + v];
+                u *= scales[(int64_t)E * N + (int64_t)e * N + cw + 4 * g + v];
+              }
+              h[v] = glu_act(act, gt) * u;
             }
-            h[v] = glu_act(act, gt) * u;
+            uint2 o;
+            o.x = pack_bf16x2(h[0], h[1]);
+            o.y = pack_bf16x2(h[2], h[3]);
+            *reinterpret_cast<uint2*>((bf16_bits*)out + (int64_t)(m0 + m) * N + cw + 4 * g) = o;
           }
-          uint2 o;
-          o.x = pack_bf16x2(h[0], h[1]);
-          o.y = pack_bf16x2(h[2], h[3]);
-          *reinterpret_cast<uint2*>((bf16_bits*)out + (int64_t)(m0 + m) * N + c0 + 4 * g) = o;
-        }
-      } else if (m < rows) {
-        float y[4];
+        } else if (m < rows) {
+          float y[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          y[v] = acc[j][v] * (W8 ? scales[2 * (int64_t)E * K + (int64_t)e * N + c0 + 4 * g + v] : 1.f);
-        float* Ys = (float*)out + (int64_t)sp * rows_cap * N;
-        *reinterpret_cast<float4*>(Ys + (int64_t)(m0 + m) * N + c0 + 4 * g) = make_float4(y[0], y[1], y[2], y[3]);
+          for (int v = 0; v < 4; ++v)
+            y[v] = acc[w][j][v] * (W8 ? scales[2 * (int64_t)E * K + (int64_t)e * N + cw + 4 * g + v] : 1.f);
+          float* Ys = (float*)out + (int64_t)sp * rows_cap * N;
+          *reinterpret_cast<float4*>(Ys + (int64_t)(m0 + m) * N + cw + 4 * g) = make_float4(y[0], y[1], y[2], y[3]);
+        }
       }
     }
   }
 }
 
-template <bool GATEUP, int MT, bool W8>
-static hipError_t stream_launch(dim3 grid, hipStream_t st, const bf16_bits* A, RouteView rv, const void* w0,
-                                const void* w1, const float* scales, int64_t T, int K, int N, int E,
+template <bool GATEUP, int MT, bool W8, int WT>
+static hipError_t stream_launch(unsigned gz, unsigned gy, hipStream_t st, const bf16_bits* A, RouteView rv,
+                                const void* w0, const void* w1, const float* scales, int64_t T, int K, int N, int E,
                                 int64_t rows_cap, int act, void* out) {
-  constexpr int lds = BsCfg<MT, W8>::kLdsBytes;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&stream_kernel<GATEUP, MT, W8>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  constexpr int lds = BsCfg<MT, W8, WT>::kLdsBytes;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&stream_kernel<GATEUP, MT, W8, WT>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((stream_kernel<GATEUP, MT, W8>), grid, dim3(kBW * 64), lds, st, A, rv, w0, w1, scales, T, K,
-                     N, E, rows_cap, act, out);
+  // one workgroup per (expert, 8 wavefronts x channels per wavefront)
+  const unsigned gx = (unsigned)E * (unsigned)(N / (kBW * (GATEUP ? 8 : 16) * WT));
+  hipLaunchKernelGGL((stream_kernel<GATEUP, MT, W8, WT>), dim3(gx, gy, gz), dim3(kBW * 64), lds, st, A, rv, w0, w1,
+                     scales, T, K, N, E, rows_cap, act, out);
   return hipGetLastError();
+}
+
+// Weight tiles per wavefront: 2 when a chunk may hold more than 32 rows of
+// 8-bit weights, so each activation fragment read from LDS feeds two MFMAs
+// (those chunks are bound by the activation fragment reads, not by HBM);
+// 1 otherwise.
+template <int MT, bool W8>
+constexpr int stream_wt() {
+  return (W8 && MT >= 4) ? 2 : 1;
 }
 
 // rows of one expert <= max_rows; chunks of 16*MT rows along grid z
 template <bool GATEUP, bool W8>
-static hipError_t stream_dispatch(int max_rows, unsigned gx, unsigned gy, hipStream_t st, const bf16_bits* A,
-                                  RouteView rv, const void* w0, const void* w1, const float* scales, int64_t T,
-                                  int K, int N, int E, int64_t rows_cap, int act, void* out) {
+static hipError_t stream_dispatch(int max_rows, unsigned gy, hipStream_t st, const bf16_bits* A, RouteView rv,
+                                  const void* w0, const void* w1, const float* scales, int64_t T, int K, int N, int E,
+                                  int64_t rows_cap, int act, void* out) {
   auto chunks = [&](int xr) { return (unsigned)((max_rows + xr - 1) / xr); };
   if (max_rows <= 16)
-    return stream_launch<GATEUP, 1, W8>(dim3(gx, gy, 1), st, A, rv, w0, w1, scales, T, K, N, E, rows_cap, act, out);
+    return stream_launch<GATEUP, 1, W8, stream_wt<1, W8>()>(1, gy, st, A, rv, w0, w1, scales, T, K, N, E, rows_cap,
+                                                            act, out);
   if (max_rows <= 32)
-    return stream_launch<GATEUP, 2, W8>(dim3(gx, gy, 1), st, A, rv, w0, w1, scales, T, K, N, E, rows_cap, act, out);
+    return stream_launch<GATEUP, 2, W8, stream_wt<2, W8>()>(1, gy, st, A, rv, w0, w1, scales, T, K, N, E, rows_cap,
+                                                            act, out);
   if (max_rows <= 64 || !W8)
-    return stream_launch<GATEUP, 4, W8>(dim3(gx, gy, chunks(64)), st, A, rv, w0, w1, scales, T, K, N, E, rows_cap,
-                                        act, out);
-  return stream_launch<GATEUP, 8, W8>(dim3(gx, gy, chunks(128)), st, A, rv, w0, w1, scales, T, K, N, E, rows_cap,
-                                      act, out);
+    return stream_launch<GATEUP, 4, W8, stream_wt<4, W8>()>(chunks(64), gy, st, A, rv, w0, w1, scales, T, K, N, E,
+                                                            rows_cap, act, out);
+  return stream_launch<GATEUP, 8, W8, stream_wt<8, W8>()>(chunks(128), gy, st, A, rv, w0, w1, scales, T, K, N, E,
+                                                          rows_cap, act, out);
 }
 
 hipError_t launch_stream_gateup(int w8, int max_rows, const bf16_bits* x, RouteView rv, const void* wg,
                                 const void* wu, const float* scales, int64_t T, int d, int f, int E, int act,
                                 bf16_bits* H, hipStream_t st) {
-  const unsigned gx = (unsigned)E * (unsigned)(f / (kBW * 8));
-  return w8 ? stream_dispatch<true, true>(max_rows, gx, 1u, st, x, rv, wg, wu, scales, T, d, f, E, 0, act, H)
-            : stream_dispatch<true, false>(max_rows, gx, 1u, st, x, rv, wg, wu, scales, T, d, f, E, 0, act, H);
+  return w8 ? stream_dispatch<true, true>(max_rows, 1u, st, x, rv, wg, wu, scales, T, d, f, E, 0, act, H)
+            : stream_dispatch<true, false>(max_rows, 1u, st, x, rv, wg, wu, scales, T, d, f, E, 0, act, H);
 }
 
 hipError_t launch_stream_down(int w8, int max_rows, int splits, const bf16_bits* H, RouteView rv, const void* wd,
                               const float* scales, int64_t rows_cap, int d, int f, int E, float* Y,
                               hipStream_t st) {
-  const unsigned gx = (unsigned)E * (unsigned)(d / (kBW * 16));
-  return w8 ? stream_dispatch<false, true>(max_rows, gx, (unsigned)splits, st, H, rv, wd, wd, scales, 0, f, d, E,
+  return w8 ? stream_dispatch<false, true>(max_rows, (unsigned)splits, st, H, rv, wd, wd, scales, 0, f, d, E,
                                            rows_cap, 0, Y)
-            : stream_dispatch<false, false>(max_rows, gx, (unsigned)splits, st, H, rv, wd, wd, scales, 0, f, d, E,
+            : stream_dispatch<false, false>(max_rows, (unsigned)splits, st, H, rv, wd, wd, scales, 0, f, d, E,
                                             rows_cap, 0, Y);
 }
 
