@@ -79,10 +79,15 @@ struct BsCfg {
   static constexpr int NI = XR / ARPI;                   // activation load instructions per stage (max)
   static constexpr int kQA = (NI + kBW - 1) / kBW;       // of which one wavefront issues at most
   static constexpr int kActOff = kBWRows * kRowB;        // activation rows follow the weight rows
-  static constexpr int kStageB = kActOff + XR * AROWB;
-  // as many stages as fit in 144 KB, at most 8
-  static constexpr int NS = 147456 / kStageB < 8 ? 147456 / kStageB : 8;
-  static constexpr int kLdsBytes = NS * kStageB;
+  static constexpr int kLdsBytes = 147456;                // ring space: 144 KB
+  // Ring of a workgroup whose chunk needs MV 16-row tiles: its stages hold
+  // only those activation rows, so fewer rows leave room for more stages
+  // (as many as fit in the ring space, at most 8).
+  template <int MV>
+  struct Ring {
+    static constexpr int kStageB = kActOff + 16 * MV * AROWB;
+    static constexpr int NS = kLdsBytes / kStageB < 8 ? kLdsBytes / kStageB : 8;
+  };
 };
 
 // slot of 16-byte chunk c of a 256-byte activation row r (16 chunks; the 16
@@ -199,11 +204,13 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
   auto run = [&](auto naw_tag, auto mv_tag) __attribute__((always_inline)) {
     constexpr int NAW = decltype(naw_tag)::value;
     constexpr int Q = 2 * WT + NAW;  // this wavefront's load instructions per stage
-    constexpr int NS = C::NS;
+    constexpr int MVT = decltype(mv_tag)::value;
+    using Rg = typename C::template Ring<MVT>;
+    constexpr int NS = Rg::NS;
     auto issue = [&](int stage, int slot) __attribute__((always_inline)) {
       int ks = stage + rot;
       if (ks >= nk) ks -= nk;
-      char* dst = lds + slot * C::kStageB;
+      char* dst = lds + slot * Rg::kStageB;
 #pragma unroll
       for (int q = 0; q < 2 * WT; ++q) dma16s(wsrc[q] + (size_t)ks * kRowB, dst + (16 * WT * wave + 8 * q) * kRowB);
 #pragma unroll
@@ -220,7 +227,7 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
       // NS, read in the previous stage, is free
       lds_barrier();
       if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
-      const char* b = lds + (kt % NS) * C::kStageB;
+      const char* b = lds + (kt % NS) * Rg::kStageB;
       if (!W8) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
