@@ -551,11 +551,116 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
   }
 }
 
+// The same permutation for at most kSmallN = 96 assignments (decode-sized
+// batches), in one wavefront: lane l holds assignments l and l + 64 of the
+// token-major list (a = t k + s). An assignment that repeats an expert of
+// its own token is a duplicate: it is not counted and shares the row of the
+// first one. The rank of assignment a of expert e is the number of counted
+// assignments of e by earlier tokens, read off the whole list with one scalar
+// lane read per assignment; counts come from LDS atomics (order-free).
+constexpr int kSmallN = 96;
+__global__ __launch_bounds__(64) void permute_small_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
+                                                           int64_t cap, int E_cap, int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ perm, int32_t* __restrict__ pos) {
+  __shared__ int s_cnt[kPermMaxE];
+  __shared__ int s_off[kPermMaxE];
+  __shared__ int s_lim[kPermMaxE];
+  __shared__ int s_idx[kSmallN];
+  const int lane = threadIdx.x;
+  const int n = T * k;
+  for (int e = lane; e < kPermMaxE; e += 64) s_cnt[e] = 0;
+  int raw[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int a = lane + 64 * j;
+    raw[j] = a < n ? idx[a] : -1;
+    if (a < n) s_idx[a] = raw[j];
+  }
+  __syncthreads();
+  int own[2], cnt[2];  // own: this assignment's expert (-1: none); cnt: the same unless a duplicate (-2)
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int a = lane + 64 * j;
+    own[j] = -1;
+    cnt[j] = -1;
+    const int e = raw[j];
+    if (a < n && e >= 0 && e < E) {
+      const int t = a / k, s = a - t * k;
+      own[j] = e;
+      cnt[j] = e;
+      for (int q = 0; q < s; ++q)
+        if (s_idx[t * k + q] == e) cnt[j] = -2;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (cnt[j] >= 0) atomicAdd(&s_cnt[cnt[j]], 1);
+  __syncthreads();
+  {
+    // exclusive scan of the capped counts: lane l owns experts kPer*l .. kPer*l + kPer - 1
+    constexpr int kPer = (kPermMaxE + 63) / 64;
+    int c[kPer], local = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = lane * kPer + j;
+      c[j] = 0;
+      if (e < E) c[j] = (cap >= 0 && e < E_cap && (int64_t)s_cnt[e] > cap) ? (int)cap : s_cnt[e];
+      local += c[j];
+    }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    int acc = incl - local;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = lane * kPer + j;
+      if (e < E) {
+        offsets[e] = acc;
+        counts[e] = c[j];
+        s_off[e] = acc;
+        s_lim[e] = c[j];
+      }
+      acc += c[j];
+    }
+    if (lane == 63) offsets[E] = incl;
+  }
+  __syncthreads();
+  // ranks: counted assignments of the same expert by earlier tokens
+  int rank[2] = {0, 0};
+  const int tk0 = (lane / k) * k, tk1 = ((lane + 64) / k) * k;  // first assignment of this lane's tokens
+  for (int b = 0; b < n; ++b) {
+    const int eb = __builtin_amdgcn_readlane(b < 64 ? cnt[0] : cnt[1], b & 63);
+    if (eb == own[0] && b < tk0) ++rank[0];
+    if (eb == own[1] && b < tk1) ++rank[1];
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int a = lane + 64 * j;
+    if (a < n) {
+      int row = -1;
+      const int e = own[j];
+      if (e >= 0 && rank[j] < s_lim[e]) {
+        row = s_off[e] + rank[j];
+        if (cnt[j] >= 0) perm[row] = (int32_t)(a / k);
+      }
+      pos[a] = row;
+    }
+  }
+}
+
 hipError_t launch_permute(const int32_t* idx, int64_t T, int E, int k, int64_t cap, int E_cap, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t stream) {
   if (E > kPermMaxE || k > kPermMaxK) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, stream, idx, T, E, k, cap, E_cap, counts, offsets, perm,
-                     pos);
+  if (T * k <= kSmallN)
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(64), 0, stream, idx, (int)T, E, k, cap, E_cap, counts,
+                       offsets, perm, pos);
+  else
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, stream, idx, T, E, k, cap, E_cap, counts, offsets,
+                       perm, pos);
   return hipGetLastError();
 }
 
