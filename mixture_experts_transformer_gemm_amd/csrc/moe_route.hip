@@ -41,6 +41,36 @@ __device__ __forceinline__ void load8_f64(const float* p, double* o) {
   o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
 }
 
+// 8 consecutive elements as loaded (bf16 bits or fp32), widened later.
+template <typename XT>
+struct Raw8;
+template <>
+struct Raw8<bf16_bits> {
+  uint4 v;
+};
+template <>
+struct Raw8<float> {
+  float4 a, b;
+};
+__device__ __forceinline__ Raw8<bf16_bits> load_raw8(const bf16_bits* p) {
+  return Raw8<bf16_bits>{*reinterpret_cast<const uint4*>(p)};
+}
+__device__ __forceinline__ Raw8<float> load_raw8(const float* p) {
+  return Raw8<float>{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
+}
+__device__ __forceinline__ void raw8_f64(const Raw8<bf16_bits>& r, double* o) {
+  const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = (double)__uint_as_float(w[i] << 16);
+    o[2 * i + 1] = (double)__uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void raw8_f64(const Raw8<float>& r, double* o) {
+  o[0] = r.a.x; o[1] = r.a.y; o[2] = r.a.z; o[3] = r.a.w;
+  o[4] = r.b.x; o[5] = r.b.y; o[6] = r.b.z; o[7] = r.b.w;
+}
+
 // One workgroup (4 wavefronts) per token, so the d-long dot products are
 // spread over 256 lanes and their loads are all in flight together. Each lane
 // accumulates 8 experts at a time over its 8-element chunks; the partials are
@@ -65,16 +95,32 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const XT* __restrict__
       double acc[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] = 0.0;
-      for (int c = threadIdx.x; c < nchunk; c += 256) {
-        double xv[8];
-        load8_f64(xr + c * 8, xv);
+      // two chunks per trip, all their loads issued before the first FMA
+      for (int c = threadIdx.x; c < nchunk; c += 512) {
+        const bool has2 = c + 256 < nchunk;
+        Raw8<XT> rx[2], rw[2][8];
+        rx[0] = load_raw8(xr + c * 8);
+        if (has2) rx[1] = load_raw8(xr + (c + 256) * 8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           if (e0 + j < E) {
-            double wv[8];
-            load8_f64(wr + (int64_t)(e0 + j) * d + c * 8, wv);
+            rw[0][j] = load_raw8(wr + (int64_t)(e0 + j) * d + c * 8);
+            if (has2) rw[1][j] = load_raw8(wr + (int64_t)(e0 + j) * d + (c + 256) * 8);
+          }
+        }
 #pragma unroll
-            for (int q = 0; q < 8; ++q) acc[j] = fma(xv[q], wv[q], acc[j]);
+        for (int u = 0; u < 2; ++u) {
+          if (u == 1 && !has2) break;
+          double xv[8];
+          raw8_f64(rx[u], xv);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if (e0 + j < E) {
+              double wv[8];
+              raw8_f64(rw[u][j], wv);
+#pragma unroll
+              for (int q = 0; q < 8; ++q) acc[j] = fma(xv[q], wv[q], acc[j]);
+            }
           }
         }
       }
