@@ -75,8 +75,8 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
     // on even when half of an expert's last tile is empty
     const int64_t r = p.rows_cap / Et;
     p.bm = r <= 32 ? 64 : (r <= 96 ? 128 : 256);
-    // 8-bit weights: one row tile per expert up to 128 rows, so each weight
-    // tile is streamed from HBM once
+    // 8-bit weights: 128-row tiles up to about 384 rows per expert (their
+    // LDS stages are smaller, so the 4-wavefront tile keeps more in flight)
     if (wdt == GROK_MOE_I8 && r <= 384) p.bm = 128;
     // split the down projection's reduction while its tiles alone would
     // leave CUs idle: (row tiles upper bound) x (d / 256) tiles per split
@@ -86,10 +86,9 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
     p.splits = s;
   }
   if (E > kFusedRouterE) {
-    // many-expert router: enough (64 x 64)-tile workgroups, each split a
-    // whole number of 64-wide reduction chunks
-    // (small T: up to one 64-wide chunk per workgroup, so the reduction is
-    // spread over the whole chip instead of looping in a few workgroups)
+    // many-expert router: its (64 tokens x 64 experts) tiles split the
+    // reduction into whole 64-wide chunks until about 256 workgroups run, so
+    // small batches spread it over the chip (down to one chunk each)
     const int64_t rtiles = ((T + 63) / 64) * ((E + 63) / 64);
     const int nchunk = (int)(d / 64);
     int s = 1;
