@@ -69,8 +69,10 @@ hipError_t launch_append_shared(const int32_t* ridx, const float* rgate, int64_t
 // E experts, k slots per token. cap >= 0: an expert e < E_cap keeps its
 // first `cap` assignments in token order, the others get pos = -1 and no
 // row; cap < 0: no cap. E <= 272, k <= 12.
+// blk: permute_scratch_ints(T, E) ints of scratch (per-block counts)
+int64_t permute_scratch_ints(int64_t T, int E);
 hipError_t launch_permute(const int32_t* idx, int64_t T, int E, int k, int64_t cap, int E_cap, int32_t* counts,
-                          int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t stream);
+                          int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* blk, hipStream_t stream);
 
 // out[t] = sum_s gate[t][s] * (sum_{p<S} Y[p][pos[t][s]]), Y: [S][rows_cap][d] fp32
 hipError_t launch_combine(int out_f32, const float* Y, int S, int64_t rows_cap, const int32_t* pos,

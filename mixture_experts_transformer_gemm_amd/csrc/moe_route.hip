@@ -432,57 +432,109 @@ hipError_t launch_append_shared(const int32_t* ridx, const float* rgate, int64_t
 }
 
 // ---------------------------------------------------------------- permutation
-// One workgroup of 1024 threads (16 wavefronts). Pass 1 counts the tokens of
-// each expert (integer LDS atomics: order-independent), one scan gives the
-// segment offsets, and pass 2 walks the tokens in chunks of 1024 in token
-// order; wave ballots give each token its rank inside its wavefront, and a
-// prefix over the wavefronts gives its rank inside the chunk. The result is a
-// stable counting sort: segment e holds its tokens in ascending order.
-// A token that lists an expert twice is counted once (both slots then point
-// at the same row); indices outside [0, E) are dropped (pos = -1).
-// With a capacity (cap >= 0; book ch. 10, section 10.3.2, the capacity
-// factor box) an assignment to a capped expert (e < E_cap: the routed ones)
-// of rank >= cap in token order is dropped too: pos = -1, no row, and the
-// segment holds the first cap.
-constexpr int kPermMaxE = 272;  // routed + shared experts
-constexpr int kPermMaxK = 12;   // slots per token
-__global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ idx, int64_t T, int E, int k,
-                                                       int64_t cap, int E_cap, int32_t* __restrict__ counts,
-                                                       int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-                                                       int32_t* __restrict__ pos) {
+// A stable counting sort of the (token, slot) assignments by expert, in three
+// launches over B blocks, each owning a contiguous chunk of tokens:
+//   count:   block b counts the assignments of each expert in its chunk (LDS
+//            integer atomics: order-independent) into blk[b][e];
+//   scan:    one workgroup turns blk[.][e] into exclusive prefixes over the
+//            blocks (the rank of block b's first assignment of expert e),
+//            caps the totals and scans them into the segment offsets;
+//   scatter: block b walks its chunk in sub-chunks of 256 tokens in token
+//            order; per wavefront and expert a 64-bit LDS mask of the lanes
+//            (tokens) that list it gives each assignment its rank inside its
+//            wavefront (earlier lanes), the masks of earlier wavefronts and
+//            the running base of the block its rank among all assignments
+//            of its expert.
+// Segment e thus holds its tokens in ascending order. A token that lists an
+// expert twice is counted once (both slots then point at the same row);
+// indices outside [0, E) are dropped (pos = -1). With a capacity (cap >= 0;
+// book ch. 10, section 10.3.2, the capacity factor box) an assignment to a
+// capped expert (e < E_cap: the routed ones) of rank >= cap in token order is
+// dropped too: pos = -1, no row, and the segment holds the first cap.
+constexpr int kPermMaxE = 272;     // routed + shared experts
+constexpr int kPermMaxK = 12;      // slots per token
+constexpr int kPermTB = 256;       // tokens per sub-chunk: one per thread
+constexpr int kPermMaxBlocks = 256;
+
+// tokens per block: whole sub-chunks, at most kPermMaxBlocks blocks
+static int64_t permute_chunk(int64_t T) {
+  const int64_t sub = (T + kPermTB - 1) / kPermTB;
+  return (sub + kPermMaxBlocks - 1) / kPermMaxBlocks * kPermTB;
+}
+
+int64_t permute_scratch_ints(int64_t T, int E) {
+  const int64_t chunk = permute_chunk(T);
+  const int64_t B = T > 0 ? (T + chunk - 1) / chunk : 1;
+  return B * (int64_t)E;
+}
+
+// the slots of token t: expert or -1 (outside [0, E)); dup[s]: slot s repeats
+// an expert of an earlier slot of the same token
+__device__ __forceinline__ void token_slots(const int32_t* __restrict__ idx, int64_t t, int E, int k,
+                                            int (&es)[kPermMaxK], bool (&dup)[kPermMaxK]) {
+#pragma unroll
+  for (int s = 0; s < kPermMaxK; ++s) {
+    es[s] = -1;
+    dup[s] = false;
+    if (s < k) {
+      const int e = idx[t * k + s];
+      es[s] = (e >= 0 && e < E) ? e : -1;
+#pragma unroll
+      for (int q = 0; q < s; ++q) dup[s] = dup[s] || (es[s] >= 0 && es[q] == es[s]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kPermTB) void permute_count_kernel(const int32_t* __restrict__ idx, int64_t T, int E,
+                                                                int k, int64_t chunk, int32_t* __restrict__ blk) {
   __shared__ int s_cnt[kPermMaxE];
-  __shared__ int s_base[kPermMaxE];  // assignments of expert e in the chunks already walked
-  __shared__ int s_off[kPermMaxE];   // first row of segment e
-  __shared__ int s_lim[kPermMaxE];   // rows segment e keeps
-  __shared__ int s_wave[16][kPermMaxE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < kPermMaxE) s_cnt[tid] = 0;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kPermTB) s_cnt[e] = 0;
   __syncthreads();
-  for (int64_t t = tid; t < T; t += 1024) {
+  const int64_t t0 = (int64_t)blockIdx.x * chunk, t1 = min(T, t0 + chunk);
+  for (int64_t t = t0 + tid; t < t1; t += kPermTB) {
     int es[kPermMaxK];
+    bool dup[kPermMaxK];
+    token_slots(idx, t, E, k, es, dup);
 #pragma unroll
-    for (int s = 0; s < kPermMaxK; ++s) {
-      es[s] = -1;
-      if (s < k) {
-        const int e = idx[t * k + s];
-        bool ok = e >= 0 && e < E;
+    for (int s = 0; s < kPermMaxK; ++s)
+      if (es[s] >= 0 && !dup[s]) atomicAdd(&s_cnt[es[s]], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kPermTB) blk[(int64_t)blockIdx.x * E + e] = s_cnt[e];
+}
+
+// one workgroup of 1024 threads: thread e < E prefixes blk[.][e] over the
+// blocks (8 loads in flight), wave 0 scans the capped totals
+__global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict__ blk, int B, int E, int64_t cap,
+                                                            int E_cap, int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets) {
+  __shared__ int s_tot[kPermMaxE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < E) {
+    int run = 0;
+    for (int b0 = 0; b0 < B; b0 += 8) {
+      int c[8];
 #pragma unroll
-        for (int q = 0; q < s; ++q) ok = ok && es[q] != e;
-        es[s] = e;
-        if (ok) atomicAdd(&s_cnt[e], 1);
+      for (int j = 0; j < 8; ++j) c[j] = b0 + j < B ? blk[(int64_t)(b0 + j) * E + tid] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (b0 + j < B) blk[(int64_t)(b0 + j) * E + tid] = run;
+        run += c[j];
       }
     }
+    s_tot[tid] = run;
   }
   __syncthreads();
   if (wave == 0) {
-    // exclusive scan of the capped counts: lane l owns experts kPer*l .. kPer*l + kPer - 1
+    // exclusive scan of the capped totals: lane l owns experts kPer*l .. kPer*l + kPer - 1
     constexpr int kPer = (kPermMaxE + 63) / 64;
     int c[kPer], local = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int e = lane * kPer + j;
       c[j] = 0;
-      if (e < E) c[j] = (cap >= 0 && e < E_cap && (int64_t)s_cnt[e] > cap) ? (int)cap : s_cnt[e];
+      if (e < E) c[j] = (cap >= 0 && e < E_cap && (int64_t)s_tot[e] > cap) ? (int)cap : s_tot[e];
       local += c[j];
     }
     int incl = local;
@@ -498,100 +550,79 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
       if (e < E) {
         offsets[e] = acc;
         counts[e] = c[j];
-        s_off[e] = acc;
-        s_lim[e] = c[j];
-        s_base[e] = 0;
       }
       acc += c[j];
     }
     if (lane == 63) offsets[E] = incl;
   }
-  __syncthreads();
+}
+
+__global__ __launch_bounds__(kPermTB) void permute_scatter_kernel(const int32_t* __restrict__ idx, int64_t T, int E,
+                                                                  int k, int64_t chunk,
+                                                                  const int32_t* __restrict__ blk,
+                                                                  const int32_t* __restrict__ counts,
+                                                                  const int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ perm,
+                                                                  int32_t* __restrict__ pos) {
+  constexpr int kWaves = kPermTB / 64;
+  __shared__ int s_base[kPermMaxE];  // assignments of expert e before the current sub-chunk
+  __shared__ int s_off[kPermMaxE];   // first row of segment e
+  __shared__ int s_lim[kPermMaxE];   // rows segment e keeps
+  // lanes of wavefront w whose token lists expert e (a token listing e twice
+  // sets its bit once)
+  __shared__ unsigned long long s_mask[kWaves][kPermMaxE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += kPermTB) {
+    s_base[e] = blk[(int64_t)blockIdx.x * E + e];
+    s_off[e] = offsets[e];
+    s_lim[e] = counts[e];
+  }
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t t0 = 0; t0 < T; t0 += 1024) {
+  const int64_t c0 = (int64_t)blockIdx.x * chunk, c1 = min(T, c0 + chunk);
+  for (int64_t t0 = c0; t0 < c1; t0 += kPermTB) {
     const int64_t t = t0 + tid;
-    int my_e[kPermMaxK], my_rank[kPermMaxK];
+    int my_e[kPermMaxK];
+    bool dup[kPermMaxK];
+    if (t < c1) {
+      token_slots(idx, t, E, k, my_e, dup);
+    } else {
 #pragma unroll
-    for (int s = 0; s < kPermMaxK; ++s) {
-      my_e[s] = -1;
-      my_rank[s] = 0;
-      if (t < T && s < k) {
-        const int e = idx[t * k + s];
-        my_e[s] = (e >= 0 && e < E) ? e : -1;
+      for (int s = 0; s < kPermMaxK; ++s) {
+        my_e[s] = -1;
+        dup[s] = false;
       }
     }
-    // ranks inside the wavefront: expert by expert over all E when the
-    // wavefront holds at least E assignments, else only over the experts
-    // present in it (the lowest unranked slot of the first lane that has one
-    // names the next), which is at most as many iterations as assignments
-    uint32_t pending = 0;
+    for (int e = lane; e < E; e += 64) s_mask[wave][e] = 0ull;
+    __syncthreads();
 #pragma unroll
     for (int s = 0; s < kPermMaxK; ++s)
-      if (my_e[s] >= 0) pending |= 1u << s;
-    int n_assign = __popc(pending);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) n_assign += __shfl_xor(n_assign, off, 64);
-    if (n_assign >= E) {
-      for (int e = 0; e < E; ++e) {
-        bool sel = false;
-#pragma unroll
-        for (int s = 0; s < kPermMaxK; ++s) sel = sel || (my_e[s] == e);
-        const uint64_t m = __ballot(sel);
-        if (lane == 0) s_wave[wave][e] = __popcll(m);
-        const int r = __popcll(m & lt_mask);
-#pragma unroll
-        for (int s = 0; s < kPermMaxK; ++s)
-          if (my_e[s] == e) my_rank[s] = r;
-      }
-      pending = 0;
-    } else {
-      for (int e = lane; e < E; e += 64) s_wave[wave][e] = 0;
-    }
-    while (true) {  // exits together: `have` is the same in every lane
-      int cand = -1;
-#pragma unroll
-      for (int s = kPermMaxK - 1; s >= 0; --s)
-        if ((pending >> s) & 1u) cand = my_e[s];
-      const uint64_t have = __ballot(cand >= 0);
-      if (have == 0) break;
-      const int e = __builtin_amdgcn_readlane(cand, __ffsll((unsigned long long)have) - 1);
-      bool sel = false;
-#pragma unroll
-      for (int s = 0; s < kPermMaxK; ++s) sel = sel || (my_e[s] == e);
-      const uint64_t m = __ballot(sel);
-      const int r = __popcll(m & lt_mask);
-#pragma unroll
-      for (int s = 0; s < kPermMaxK; ++s)
-        if (my_e[s] == e) {
-          my_rank[s] = r;
-          pending &= ~(1u << s);
-        }
-      if (lane == 0) s_wave[wave][e] = __popcll(m);
-    }
+      if (my_e[s] >= 0) atomicOr(&s_mask[wave][my_e[s]], 1ull << lane);
     __syncthreads();
-    if (t < T) {
+    // rank = earlier sub-chunks and blocks + earlier wavefronts of this
+    // sub-chunk + earlier lanes of this wavefront
+    if (t < c1) {
 #pragma unroll
       for (int s = 0; s < kPermMaxK; ++s) {
         if (s >= k) break;
         const int e = my_e[s];
         int row = -1;
         if (e >= 0) {
-          int pre = 0;
-          for (int w = 0; w < wave; ++w) pre += s_wave[w][e];
-          const int rank = s_base[e] + pre + my_rank[s];
+          int rank = s_base[e] + __popcll(s_mask[wave][e] & lt_mask);
+          for (int w = 0; w < wave; ++w) rank += __popcll(s_mask[w][e]);
           if (rank < s_lim[e]) {
             row = s_off[e] + rank;
-            perm[row] = (int32_t)t;
+            if (!dup[s]) perm[row] = (int32_t)t;
           }
         }
         pos[t * k + s] = row;
       }
     }
     __syncthreads();
-    if (tid < E) {
+    for (int e = tid; e < E; e += kPermTB) {
       int tot = 0;
-      for (int w = 0; w < 16; ++w) tot += s_wave[w][tid];
-      s_base[tid] += tot;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) tot += __popcll(s_mask[w][e]);
+      s_base[e] += tot;
     }
     __syncthreads();
   }
@@ -699,14 +730,19 @@ __global__ __launch_bounds__(64) void permute_small_kernel(const int32_t* __rest
 }
 
 hipError_t launch_permute(const int32_t* idx, int64_t T, int E, int k, int64_t cap, int E_cap, int32_t* counts,
-                          int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t stream) {
+                          int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* blk, hipStream_t stream) {
   if (E > kPermMaxE || k > kPermMaxK) return hipErrorInvalidValue;
-  if (T * k <= kSmallN)
+  if (T * k <= kSmallN) {
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(64), 0, stream, idx, (int)T, E, k, cap, E_cap, counts,
                        offsets, perm, pos);
-  else
-    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, stream, idx, T, E, k, cap, E_cap, counts, offsets,
-                       perm, pos);
+    return hipGetLastError();
+  }
+  const int64_t chunk = permute_chunk(T);
+  const int B = (int)((T + chunk - 1) / chunk);
+  hipLaunchKernelGGL(permute_count_kernel, dim3(B), dim3(kPermTB), 0, stream, idx, T, E, k, chunk, blk);
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, stream, blk, B, E, cap, E_cap, counts, offsets);
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3(B), dim3(kPermTB), 0, stream, idx, T, E, k, chunk, blk, counts,
+                     offsets, perm, pos);
   return hipGetLastError();
 }
 

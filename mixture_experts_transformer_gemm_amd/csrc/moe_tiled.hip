@@ -96,16 +96,6 @@ __device__ __forceinline__ const bf16_bits* act_row(const bf16_bits* A, const Ro
   return A + (int64_t)(t.m0 + r) * K;
 }
 
-// Weight row r (0..255) of the tile: gate channels then up channels for the
-// gate/up pass, 256 down channels otherwise.
-template <bool GATEUP>
-__device__ __forceinline__ const char* weight_row(const void* w0, const void* w1, const Tile& t, int N, int K,
-                                                  size_t wsz, int r) {
-  const char* base = (const char*)((GATEUP && r >= TBN / 2) ? w1 : w0);
-  const int ch = t.n0 + (GATEUP ? (r & (TBN / 2 - 1)) : r);
-  return base + ((int64_t)t.e * N + ch) * (int64_t)K * wsz;
-}
-
 // Scales each accumulator by its channel's 8-bit-weight scale (W8), forms
 // GELU(gate) * up (gate/up pass, bf16 H) or stores the fp32 down product.
 template <int BM, bool GATEUP, bool W8, int NW = 4>
@@ -271,32 +261,55 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
   // source of each of this lane's load instructions (stage 0): QA activation
   // instructions, then QW weight instructions. Activation instruction q holds
   // tile rows [q ARPI NW, (q + 1) ARPI NW); those wholly past the segment's
-  // end are not issued (qav of them are).
+  // end are not issued (qav of them are). Sources inside one tile are a
+  // workgroup-uniform base plus a 32-bit per-lane offset (weight rows and the
+  // down pass's contiguous H rows); gathered token rows keep full pointers.
   const int qav = min(D::QA, (t.M + D::ARPI * NW - 1) / (D::ARPI * NW));
-  const char* src[D::Q];
+  constexpr int wsz = W8 ? 1 : 2;
+  const char* abase = (const char*)(A + (int64_t)t.m0 * K + kbeg);  // down pass
+  const char* agather[GATEUP ? D::QA : 1];
+  uint32_t aoff[GATEUP ? 1 : D::QA];
 #pragma unroll
   for (int q = 0; q < D::QA; ++q) {
     const int R = D::ARPI * (q * NW + wave) + lane / D::ACH;
     const int c = dslot<D::AROWB>(R, lane % D::ACH);
-    src[q] = (const char*)(act_row<GATEUP>(A, rv, t, T, K, R) + kbeg) + c * 16;
+    if constexpr (GATEUP)
+      agather[q] = (const char*)(act_row<GATEUP>(A, rv, t, T, K, R) + kbeg) + c * 16;
+    else
+      aoff[q] = (uint32_t)(min(R, t.M - 1) * (K * 2) + c * 16);
   }
+  // weight rows: gate channels [n0, n0 + 128) then up channels for the
+  // gate/up pass (instruction q reads up rows when q ARPI NW >= 128, the same
+  // for every lane), 256 down channels otherwise
+  const int64_t wrow0 = ((int64_t)t.e * N + t.n0) * K + kbeg;
+  const char* wbase0 = (const char*)w0 + wrow0 * wsz;
+  const char* wbase1 = (const char*)w1 + wrow0 * wsz;
+  uint32_t woff[D::QW];
 #pragma unroll
   for (int q = 0; q < D::QW; ++q) {
     const int R = D::WRPI * (q * NW + wave) + lane / D::WCH;
     const int c = dslot<D::WROWB>(R, lane % D::WCH);
-    src[D::QA + q] = weight_row<GATEUP>(w0, w1, t, N, K, W8 ? 1 : 2, R) + (size_t)kbeg * (W8 ? 1 : 2) + c * 16;
+    woff[q] = (uint32_t)((R & (GATEUP ? TBN / 2 - 1 : TBN - 1)) * (K * wsz) + c * 16);
   }
   auto issue_act = [&](int stage, int buf) {
     char* dst = lds + buf * D::kStageBytes;
 #pragma unroll
-    for (int q = 0; q < D::QA; ++q)
-      if (q < qav) dma16(src[q] + (size_t)stage * D::AROWB, dst + (q * NW + wave) * 1024);
+    for (int q = 0; q < D::QA; ++q) {
+      if (q < qav) {
+        if constexpr (GATEUP)
+          dma16(agather[q] + (size_t)stage * D::AROWB, dst + (q * NW + wave) * 1024);
+        else
+          dma16(abase + (size_t)stage * D::AROWB + aoff[q], dst + (q * NW + wave) * 1024);
+      }
+    }
   };
   auto issue_w = [&](int stage, int buf) {
     char* dst = lds + buf * D::kStageBytes;
 #pragma unroll
-    for (int q = 0; q < D::QW; ++q)
-      dma16(src[D::QA + q] + (size_t)stage * D::WROWB, dst + D::kActBytes + (q * NW + wave) * 1024);
+    for (int q = 0; q < D::QW; ++q) {
+      const bool up = GATEUP && q * D::WRPI * NW >= TBN / 2;
+      dma16((up ? wbase1 : wbase0) + (size_t)stage * D::WROWB + woff[q], dst + D::kActBytes + (q * NW + wave) * 1024);
+    }
   };
   // stage k has landed when at most NS-2 later stages of this wavefront's
   // loads (qav + QW instructions each) are in flight; lgkmcnt(0) as well
@@ -414,10 +427,14 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
   } else if (tjv == 1) {
     stage_loop(std::integral_constant<int, 1>{});
   } else if constexpr (C::TJ > 2) {
-    if (tjv == 2)
+    if (tjv == 2) {
       stage_loop(std::integral_constant<int, 2>{});
-    else
-      stage_loop(std::integral_constant<int, (C::TJ > 3 ? 3 : 2)>{});
+    } else if constexpr (C::TJ > 3) {
+      if (tjv == 3)
+        stage_loop(std::integral_constant<int, 3>{});
+      else if constexpr (C::TJ > 4)
+        stage_loop(std::integral_constant<int, 4>{});  // tjv == 4 < TJ == 5
+    }
   }
   // drain the (duplicate) loads still in flight before the workgroup exits
   GMOE_WAIT_VM_LGKM0(0);
@@ -439,7 +456,7 @@ static unsigned tiled_blocks(int bm, int64_t rows_cap, int E, int nN) {
 // in 144 KB, at most 6.
 template <int BM, bool W8>
 struct DmaChoice {
-  static constexpr int NW = BM == 256 ? 8 : 4;
+  static constexpr int NW = BM >= 256 ? 8 : 4;
   static constexpr int kStage = DmaCfg<BM, NW, 2, W8>::kStageBytes;
   static constexpr int NS = 147456 / kStage < 6 ? 147456 / kStage : 6;
 };
@@ -478,6 +495,9 @@ static hipError_t tiled_dispatch(bool w8, int bm, hipStream_t st, const bf16_bit
       return tiled_launch<128, GATEUP>(w8, st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, act, out);
     case 256:
       return tiled_launch<256, GATEUP>(w8, st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, act, out);
+    case 320:  // bf16 weights only (the 8-bit instance would not fit in registers)
+      if (w8) return hipErrorInvalidValue;
+      return launch_dma<320, GATEUP, false>(st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, act, out);
   }
   return hipErrorInvalidValue;
 }

@@ -187,3 +187,32 @@ def test_router_sends_every_token_to_two_experts(T):
     got, dbg, _ = _full_check(w)
     assert (dbg["idx"] == [0, 5]).all()
     assert list(dbg["counts"]) == [T, 0, 0, 0, 0, T, 0, 0]
+
+
+@pytest.mark.parametrize("E,k,cf", [(8, 2, 0.0), (256, 8, 0.0), (8, 2, 0.9), (256, 8, 1.1)])
+def test_permutation_many_blocks(E, k, cf):
+    # 70,000 tokens: more than 256 sub-chunks of 256 tokens, so each permutation block walks two
+    # sub-chunks (the last one ragged). Caller routing with skewed expert popularity (weighted
+    # sampling of k distinct experts per token); permutation bit-exact against the oracle's, with
+    # and without a capacity cap; outputs checked on a sample of tokens
+    T = 70000
+    w = synthetic.make("decode", T=T, d=256, f=256, E=E, k=k, seed=E + k, capacity_factor=cf)
+    rng = np.random.default_rng(E * 31 + k)
+    weight = 1.0 / (1.0 + np.arange(E)) ** 0.7
+    keys = np.log(rng.random((T, E))) / weight                 # top-k keys: sampling without replacement
+    idx = np.argsort(-keys, axis=1, kind="stable")[:, :k].astype(np.int32)
+    gate = rng.random((T, k)).astype(np.float32)
+    got, dbg = run_layer(w, torch, route_idx=idx, route_gate=gate)
+    cap = oracle.capacity(cf, T, E, k)
+    c, o, p, pos = oracle.permute_cap(idx, E, cap)
+    np.testing.assert_array_equal(dbg["counts"], c)
+    np.testing.assert_array_equal(dbg["offsets"], o)
+    np.testing.assert_array_equal(dbg["perm"][:o[-1]], p[:o[-1]])
+    np.testing.assert_array_equal(dbg["pos"], pos)
+    if cf > 0:
+        assert c.max() == cap and (pos < 0).any()
+    toks = np.sort(rng.choice(T, 256, replace=False))
+    # dropped assignments contribute nothing: gate 0 in the oracle
+    ref = oracle.forward_given_routing(w.x, w.w_gate, w.w_up, w.w_down, idx,
+                                       np.where(pos >= 0, gate, 0.0).astype(np.float64), tokens=toks)
+    assert normwise_err(got[toks], ref) <= TOL["bf16"]
