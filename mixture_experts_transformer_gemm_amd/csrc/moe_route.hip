@@ -203,85 +203,130 @@ hipError_t launch_router(int act_f32, const void* x, const void* router_w, int64
 // ---------------------------------------------------------------- many-expert router (E > 64)
 // Fine-grained layers route over hundreds of experts (256 in DeepSeek-V3,
 // book ch. 10, section 10.1 table). The logits become a [T][E] GEMM in two
-// kernels: router_gemm_kernel forms split-K partial logits in fp64 (each
+// kernels: router_mfma_kernel forms split-K partial logits in fp64 (each
 // bf16 product is exact in fp64), router_topk_block_kernel sums the
 // partials in split order and runs softmax and top-k with one workgroup per
 // token.
 
-// Workgroup tile: 64 tokens x 64 experts, reduction chunks of 64 staged as
-// bf16 in LDS (rows padded to 72 values, so the 16 rows that a wavefront
-// reads at once fall into distinct banks). Thread (tm, tn) owns tokens
-// tm + 16i and experts tn + 16j (i, j < 4); grid z splits the reduction.
-constexpr int kRgTile = 64, kRgK = 64, kRgLd = kRgK + 8;
+// Workgroup tile: 64 tokens x 256 experts (wavefront w: experts 64 w ..
+// 64 w + 63), reduction chunks of 64 staged as bf16 in LDS (rows padded to 72
+// values, so the 16 rows that a wavefront reads at once start in distinct
+// banks); the next chunk is loaded into registers while this one is used.
+// Products on v_mfma_f64_16x16x4f64 (A: 16 tokens x 4, B: 4 x 16 experts;
+// lane l supplies row l mod 16 and reduction index l / 16 of each; result
+// value v of lane l is C[l / 16 + 4 v][l mod 16], measured). Inside each block of 16
+// reduction values, lane group g = l / 16 reads the 4 consecutive values
+// [4 g, 4 g + 4) of its row once and feeds value q to MFMA q, so MFMA q sums
+// the indices 4 g + q over g, the same ones on both operands: every product
+// is exact in fp64 and only the order of the fp64 sum differs from a
+// sequential one. Grid z splits the reduction (partials in P[z]).
+constexpr int kRmTok = 64, kRmExp = 256, kRmK = 64, kRmLd = kRmK + 8;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void bf16x8_to_f64(uint4 v, double* o) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+__device__ __forceinline__ double bf16_lo_f64(uint32_t w) { return (double)__uint_as_float(w << 16); }
+__device__ __forceinline__ double bf16_hi_f64(uint32_t w) { return (double)__uint_as_float(w & 0xFFFF0000u); }
+
+// one staged chunk for a tile whose first NTB blocks of 16 tokens hold tokens
+template <int NTB>
+__device__ __forceinline__ void router_mfma_chunk(const bf16_bits* sx, const bf16_bits* sw, int lane, int wave,
+                                                  f64x4 (&acc)[4][4]) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll 1
+  for (int kb = 0; kb < kRmK; kb += 16) {
+    uint2 ra[NTB], rb[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o[2 * i] = (double)__uint_as_float(w[i] << 16);
-    o[2 * i + 1] = (double)__uint_as_float(w[i] & 0xFFFF0000u);
+    for (int i = 0; i < NTB; ++i) ra[i] = *reinterpret_cast<const uint2*>(sx + (16 * i + r) * kRmLd + kb + 4 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      rb[j] = *reinterpret_cast<const uint2*>(sw + (64 * wave + 16 * j + r) * kRmLd + kb + 4 * g);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      double a[NTB], b[4];
+#pragma unroll
+      for (int i = 0; i < NTB; ++i) {
+        const uint32_t w = (q < 2) ? ra[i].x : ra[i].y;
+        a[i] = (q & 1) ? bf16_hi_f64(w) : bf16_lo_f64(w);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = (q < 2) ? rb[j].x : rb[j].y;
+        b[j] = (q & 1) ? bf16_hi_f64(w) : bf16_lo_f64(w);
+      }
+#pragma unroll
+      for (int i = 0; i < NTB; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
   }
 }
 
-__global__ __launch_bounds__(256) void router_gemm_kernel(const bf16_bits* __restrict__ x,
+__global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_bits* __restrict__ x,
                                                           const bf16_bits* __restrict__ wr, int64_t T, int d, int E,
                                                           double* __restrict__ P) {
-  __shared__ __attribute__((aligned(16))) bf16_bits sx[kRgTile * kRgLd];
-  __shared__ __attribute__((aligned(16))) bf16_bits sw[kRgTile * kRgLd];
-  const int tid = threadIdx.x, tn = tid & 15, tm = tid >> 4;
-  const int64_t t0 = (int64_t)blockIdx.x * kRgTile;
-  const int e0 = blockIdx.y * kRgTile;
-  const int kspan = d / (int)gridDim.z, kbeg = (int)blockIdx.z * kspan;
-  double acc[4][4];
+  __shared__ __attribute__((aligned(16))) bf16_bits sx[kRmTok * kRmLd];
+  __shared__ __attribute__((aligned(16))) bf16_bits sw[kRmExp * kRmLd];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * kRmTok;
+  const int e0 = blockIdx.y * kRmExp;
+  const int kspan = d / (int)gridDim.z, kbeg = (int)blockIdx.z * kspan, kend = kbeg + kspan;
+  const int64_t rows = T - t0;
+  const int ntb = rows >= 64 ? 4 : (int)((rows + 15) / 16);
+  f64x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-  for (int kc = kbeg; kc < kbeg + kspan; kc += kRgK) {
-    // 64 rows x 64 values of each operand: 512 16-byte pieces, 2 per thread
-    uint4 vx[2], vw[2];
+    for (int j = 0; j < 4; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  // 16-byte pieces: x 64 rows x 8 (2 per thread), weights 256 rows x 8 (8 per thread)
+  uint4 vx[2], vw[8];
+  auto load = [&](int kc) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int lin = tid + 256 * q, r = lin >> 3, c = (lin & 7) * 8;
-      const int64_t tok = t0 + r;
-      const int e = e0 + r;
+      const int lin = tid + 256 * q, rr = lin >> 3, c = (lin & 7) * 8;
+      const int64_t tok = t0 + rr;
       vx[q] = tok < T ? *reinterpret_cast<const uint4*>(x + tok * d + kc + c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int lin = tid + 256 * q, rr = lin >> 3, c = (lin & 7) * 8;
+      const int e = e0 + rr;
       vw[q] = e < E ? *reinterpret_cast<const uint4*>(wr + (int64_t)e * d + kc + c) : make_uint4(0, 0, 0, 0);
     }
+  };
+  load(kbeg);
+  for (int kc = kbeg; kc < kend; kc += kRmK) {
     __syncthreads();  // the previous chunk's reads are done
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int lin = tid + 256 * q, r = lin >> 3, c = (lin & 7) * 8;
-      *reinterpret_cast<uint4*>(sx + r * kRgLd + c) = vx[q];
-      *reinterpret_cast<uint4*>(sw + r * kRgLd + c) = vw[q];
+      const int lin = tid + 256 * q;
+      *reinterpret_cast<uint4*>(sx + (lin >> 3) * kRmLd + (lin & 7) * 8) = vx[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int lin = tid + 256 * q;
+      *reinterpret_cast<uint4*>(sw + (lin >> 3) * kRmLd + (lin & 7) * 8) = vw[q];
     }
     __syncthreads();
-#pragma unroll 2
-    for (int k8 = 0; k8 < kRgK; k8 += 8) {
-      double xv[4][8], wv[4][8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bf16x8_to_f64(*reinterpret_cast<const uint4*>(sx + (tm + 16 * i) * kRgLd + k8), xv[i]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bf16x8_to_f64(*reinterpret_cast<const uint4*>(sw + (tn + 16 * j) * kRgLd + k8), wv[j]);
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = fma(xv[i][q], wv[j][q], acc[i][j]);
+    if (kc + kRmK < kend) load(kc + kRmK);
+    switch (ntb) {
+      case 4: router_mfma_chunk<4>(sx, sw, lane, wave, acc); break;
+      case 3: router_mfma_chunk<3>(sx, sw, lane, wave, acc); break;
+      case 2: router_mfma_chunk<2>(sx, sw, lane, wave, acc); break;
+      default: router_mfma_chunk<1>(sx, sw, lane, wave, acc); break;
     }
   }
   double* Ps = P + (int64_t)blockIdx.z * T * E;
+  const int r = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t tok = t0 + tm + 16 * i;
-    if (tok >= T) continue;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tn + 16 * j;
-      if (e < E) Ps[tok * E + e] = acc[i][j];
+      const int e = e0 + 64 * wave + 16 * j + r;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t tok = t0 + 16 * i + g + 4 * v;
+        if (tok < T && e < E) Ps[tok * E + e] = acc[i][j][v];
+      }
     }
-  }
 }
 
 // One workgroup per token, thread e holding expert e (E <= 256): the split
@@ -390,8 +435,8 @@ __global__ __launch_bounds__(256) void router_topk_block_kernel(const double* __
 hipError_t launch_router_many(const bf16_bits* x, const bf16_bits* router_w, int64_t T, int d, int E, int k, int ns,
                               int renorm, const float* bias, int splits, double* P, int32_t* idx, float* gate,
                               hipStream_t stream) {
-  const dim3 grid((unsigned)((T + kRgTile - 1) / kRgTile), (unsigned)((E + kRgTile - 1) / kRgTile), (unsigned)splits);
-  hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(256), 0, stream, x, router_w, T, d, E, P);
+  const dim3 grid((unsigned)((T + kRmTok - 1) / kRmTok), (unsigned)((E + kRmExp - 1) / kRmExp), (unsigned)splits);
+  hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(256), 0, stream, x, router_w, T, d, E, P);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   int64_t blocks = T < 16384 ? T : 16384;
