@@ -8,9 +8,10 @@
 // Down pass: Y = H Wd^T -> fp32.
 //
 // Workgroup tile: BM rows x 256 weight rows (BM = 64 or 128 with 4
-// wavefronts, 256 with 8). For the gate/up pass the 256 weight rows are 128
-// gate channels and the same 128 up channels, so act(gate) * up is formed in
-// registers. Products use v_mfma_f32_32x32x16_bf16 with the weight fragment
+// wavefronts, 256 or 320 with 8). For the gate/up pass the 256 weight rows
+// are 128 gate channels and the same 128 up channels, so act(gate) * up is
+// formed in registers. With two wavefront rows, row subtile q (32 rows) goes
+// to wavefront row q mod 2, so a partly filled tile keeps both busy. Products use v_mfma_f32_32x32x16_bf16 with the weight fragment
 // as the "A" operand (32 channels) and the activation fragment as "B" (32
 // rows): lane l supplies row (l mod 32) and the 8 reduction values of group
 // l / 32; result register v of lane l is C[8 (v / 4) + 4 (l / 32) + (v mod
@@ -122,7 +123,7 @@ __device__ __forceinline__ void epilogue(AccT<BM, NW>& acc, const Tile& t,
         }
 #pragma unroll
         for (int j = 0; j < C::TJ; ++j) {
-          const int m = wm * C::RW + j * 32 + r32;
+          const int m = (j * C::WM + wm) * 32 + r32;
           if (m < t.M) {
             float h[4];
 #pragma unroll
@@ -149,7 +150,7 @@ __device__ __forceinline__ void epilogue(AccT<BM, NW>& acc, const Tile& t,
         }
 #pragma unroll
         for (int j = 0; j < C::TJ; ++j) {
-          const int m = wm * C::RW + j * 32 + r32;
+          const int m = (j * C::WM + wm) * 32 + r32;
           if (m < t.M) {
             const float4 o = make_float4(acc[i][j][4 * q] * s0[0], acc[i][j][4 * q + 1] * s0[1],
                                          acc[i][j][4 * q + 2] * s0[2], acc[i][j][4 * q + 3] * s0[3]);
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
         const int cx = W8 ? (2 * (s & ~1) + 2 * hg + (s & 1)) : (2 * s + hg);
 #pragma unroll
         for (int j = 0; j < TJV; ++j) {
-          const int R = wm * C::RW + j * 32 + r32;
+          const int R = (j * C::WM + wm) * 32 + r32;
           xa[j] = *reinterpret_cast<const u32x4*>(b + R * D::AROWB + dslot<D::AROWB>(R, cx) * 16);
         }
       }
@@ -418,8 +419,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  const int valid_rows = t.M - wm * C::RW;
-  const int tjv = valid_rows <= 0 ? 0 : min(C::TJ, (valid_rows + 31) / 32);
+  // row subtiles j * WM + wm (j < TJ) belong to wavefront row wm, so a
+  // partly filled tile spreads its rows over both wavefront rows
+  const int nsub = (t.M + 31) / 32;
+  const int tjv = nsub <= wm ? 0 : min(C::TJ, (nsub - wm + C::WM - 1) / C::WM);
   if (tjv >= C::TJ) {
     stage_loop(std::integral_constant<int, C::TJ>{});
   } else if (tjv == 0) {
