@@ -28,6 +28,8 @@ struct Plan {
   int rsplits = 0; // split-K factor of the many-expert router GEMM (0: fused router)
   int64_t rows_cap = 0;
   size_t off_idx = 0, off_gate = 0, off_counts = 0, off_offsets = 0, off_perm = 0, off_pos = 0, off_pblk = 0;
+  size_t off_tiles = 0;
+  int64_t mt_ub = 0;  // tiled path: tiles of bm rows, at most rows_cap / bm + Et
   size_t off_logits = 0, off_U = 0, off_H = 0, off_Y = 0, total = 0;
 };
 
@@ -111,6 +113,8 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
   p.off_perm = o;    o = align256(o + sizeof(int32_t) * (size_t)(T * K));
   p.off_pos = o;     o = align256(o + sizeof(int32_t) * (size_t)(T * K));
   p.off_pblk = o;    o = align256(o + sizeof(int32_t) * (size_t)permute_scratch_ints(T, Et));
+  if (p.path == PATH_TILED) p.mt_ub = p.rows_cap / p.bm + Et;
+  p.off_tiles = o;   o = align256(o + sizeof(int32_t) * (size_t)(Et + 1 + p.mt_ub));  // tile_off, tile_e
   p.off_logits = o;  o = align256(o + sizeof(double) * (size_t)p.rsplits * (size_t)T * (size_t)E);
   p.off_U = o;       o = align256(o + (act == GROK_MOE_F32 ? 4 : 2) * (size_t)T * (size_t)d);  // sandwich pre-norm
   p.off_H = o;       o = align256(o + hsz * (size_t)p.rows_cap * (size_t)f);
@@ -240,7 +244,14 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
   if (!record(dbg, 1, st)) return GROK_MOE_EHIP;
   GMOE_TRY(launch_permute(ridx, T, E, k, capacity_rows(a->capacity_factor, T, Er, kr), Er, counts, offsets, perm, pos,
                           pblk, st));
-  const RouteView rv{counts, offsets, perm};
+  RouteView rv{counts, offsets, perm, nullptr, nullptr};
+  if (p.path == PATH_TILED) {
+    int32_t* tile_off = (int32_t*)(w + p.off_tiles);
+    int32_t* tile_e = tile_off + (E + 1);
+    GMOE_TRY(launch_tile_table(counts, E, p.bm, tile_off, tile_e, p.mt_ub, st));
+    rv.tile_off = tile_off;
+    rv.tile_e = tile_e;
+  }
 
   // stage 2: gate/up projections + GELU * up
   if (!record(dbg, 2, st)) return GROK_MOE_EHIP;

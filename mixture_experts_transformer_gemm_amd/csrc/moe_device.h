@@ -54,25 +54,6 @@ __device__ __forceinline__ void load_wfrags(const void* wrow, int kb, int g, u32
   }
 }
 
-// Finds the M tile `mt` (tiles of BM rows, experts in order). Returns the
-// expert or -1 when mt is past the last tile.
-template <int BM>
-__device__ __forceinline__ int find_tile(const RouteView& rv, int E, int mt, int& m0, int& M) {
-  int acc = 0;
-  for (int q = 0; q < E; ++q) {
-    const int c = rv.counts[q];
-    const int nt = (c + BM - 1) / BM;
-    if (mt < acc + nt) {
-      const int mloc = (mt - acc) * BM;
-      m0 = rv.offsets[q] + mloc;
-      M = min(BM, c - mloc);
-      return q;
-    }
-    acc += nt;
-  }
-  return -1;
-}
-
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {

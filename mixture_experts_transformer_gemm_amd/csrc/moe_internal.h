@@ -43,6 +43,9 @@ struct RouteView {
   const int32_t* counts;   // [E] rows per expert
   const int32_t* offsets;  // [E+1] first row of each expert segment
   const int32_t* perm;     // [k*T] row -> token
+  // tiled path only (else null): tiles of BM rows, experts in order
+  const int32_t* tile_off;  // [E+1] first tile of each expert; tile_off[E] = tiles
+  const int32_t* tile_e;    // [tiles] expert of each tile
 };
 
 // ---------------------------------------------------------------- launchers
@@ -69,6 +72,10 @@ hipError_t launch_append_shared(const int32_t* ridx, const float* rgate, int64_t
 // E experts, k slots per token. cap >= 0: an expert e < E_cap keeps its
 // first `cap` assignments in token order, the others get pos = -1 and no
 // row; cap < 0: no cap. E <= 272, k <= 12.
+// tile_off[e] = sum over q < e of ceil(counts[q] / bm) (e <= E) and
+// tile_e[m] = the expert of tile m, for the tile_off[E] <= mt_ub tiles
+hipError_t launch_tile_table(const int32_t* counts, int E, int bm, int32_t* tile_off, int32_t* tile_e, int64_t mt_ub,
+                             hipStream_t stream);
 // blk: permute_scratch_ints(T, E) ints of scratch (per-block counts)
 int64_t permute_scratch_ints(int64_t T, int E);
 hipError_t launch_permute(const int32_t* idx, int64_t T, int E, int k, int64_t cap, int E_cap, int32_t* counts,

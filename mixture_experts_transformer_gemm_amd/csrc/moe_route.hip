@@ -791,6 +791,65 @@ hipError_t launch_permute(const int32_t* idx, int64_t T, int E, int k, int64_t c
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- tile table
+// The tiled GEMMs walk tiles of bm rows over the expert segments in order.
+// One workgroup: wavefront 0 scans the per-expert tile counts into tile_off,
+// then every thread fills tile_e for a stride of tiles by binary search.
+__global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restrict__ counts, int E, int bm,
+                                                          int32_t* __restrict__ tile_off, int32_t* __restrict__ tile_e,
+                                                          int64_t mt_ub) {
+  __shared__ int s_off[kPermMaxE + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 64) {
+    constexpr int kPer = (kPermMaxE + 63) / 64;
+    int c[kPer], local = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = lane * kPer + j;
+      c[j] = e < E ? (counts[e] + bm - 1) / bm : 0;
+      local += c[j];
+    }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    int acc = incl - local;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = lane * kPer + j;
+      if (e < E) {
+        s_off[e] = acc;
+        tile_off[e] = acc;
+      }
+      acc += c[j];
+    }
+    if (lane == 63) {
+      s_off[E] = incl;
+      tile_off[E] = incl;
+    }
+  }
+  __syncthreads();
+  const int total = (int)min((int64_t)s_off[E], mt_ub);
+  for (int m = tid; m < total; m += 1024) {
+    int lo = 0, hi = E - 1;  // the last e with s_off[e] <= m
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= m) lo = mid;
+      else hi = mid - 1;
+    }
+    tile_e[m] = lo;
+  }
+}
+
+hipError_t launch_tile_table(const int32_t* counts, int E, int bm, int32_t* tile_off, int32_t* tile_e, int64_t mt_ub,
+                             hipStream_t stream) {
+  if (E > kPermMaxE || bm <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, stream, counts, E, bm, tile_off, tile_e, mt_ub);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- combine
 // out[t][n] = sum over slots s (slot order) of gate[t][s] * y_s[n], where y_s
 // is the down-projection row of assignment (t, s) summed over the split-K

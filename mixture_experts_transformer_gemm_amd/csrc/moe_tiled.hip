@@ -64,8 +64,7 @@ template <int BM, bool GATEUP>
 __device__ __forceinline__ bool select_tile(const RouteView& rv, int E, int N, Tile& t, int slot) {
   constexpr int kTileCh = GATEUP ? TBN / 2 : TBN;  // output channels per tile
   const int nN = N / kTileCh;
-  int mtiles = 0;
-  for (int q = 0; q < E; ++q) mtiles += (rv.counts[q] + BM - 1) / BM;
+  const int mtiles = rv.tile_off[E];
   const int total = mtiles * nN;
   const int per_xcd = (total + 7) >> 3;
   const int xcd = blockIdx.x & 7;
@@ -78,9 +77,12 @@ __device__ __forceinline__ bool select_tile(const RouteView& rv, int E, int N, T
   const int within = L - group * kGroupM * nN;
   const int mt = first_m + within % gsz;
   const int nt = within / gsz;
-  t.e = find_tile<BM>(rv, E, mt, t.m0, t.M);
+  t.e = rv.tile_e[mt];
+  const int mloc = (mt - rv.tile_off[t.e]) * BM;
+  t.m0 = rv.offsets[t.e] + mloc;
+  t.M = min(BM, rv.counts[t.e] - mloc);
   t.n0 = nt * kTileCh;
-  return t.e >= 0;
+  return true;
 }
 
 // Row pointer of tile row r (clamped into the segment): the token's row of x
