@@ -61,13 +61,16 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
   } else if ((wdt == GROK_MOE_BF16 && T <= kStreamMaxT) || (wdt == GROK_MOE_I8 && T <= kStream8MaxT)) {
     p.path = PATH_STREAM;
     p.mt_max = (int)T;  // rows of one expert <= T
-    // enough workgroups (of 128 output channels) for the down projection,
-    // about 3-4 per CU (measured at decode: 768 workgroups stream the down
-    // weights 3-5% faster than 1536 or 384); each split keeps whole stages
-    // (64 bf16 or 128 8-bit reduction values)
+    // enough workgroups for the down projection, about 3 per CU (measured
+    // at decode: 768 workgroups stream the down weights 3-5% faster than
+    // 1536 or 384 with bf16 weights, and 19% faster than 384 with 8-bit
+    // ones); a workgroup covers 128 output channels (bf16) or 256 (8-bit
+    // weights, two weight tiles per wavefront), and each split keeps whole
+    // stages (64 bf16 or 128 8-bit reduction values)
     const int64_t ks = wdt == GROK_MOE_I8 ? 128 : 64;
+    const int64_t ch_per_wg = wdt == GROK_MOE_I8 ? 256 : 128;
     int s = 1;
-    while (s < 8 && (int64_t)Et * (d / 64) * s < 1024 && (f / (2 * s)) % ks == 0) s *= 2;
+    while (s < 8 && (int64_t)Et * (d / ch_per_wg) * s < 512 && (f / (2 * s)) % ks == 0) s *= 2;
     p.splits = s;
   } else {
     p.path = PATH_TILED;

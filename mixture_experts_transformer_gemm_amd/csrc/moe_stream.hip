@@ -342,15 +342,16 @@ static hipError_t stream_launch(unsigned gz, unsigned gy, hipStream_t st, const 
   return hipGetLastError();
 }
 
-// Weight tiles per wavefront: 2 for 8-bit weights in the gate/up pass and
-// in down chunks of more than 32 rows, 1 otherwise. Chunks of more than 32
-// rows are bound by the activation fragment reads, which then feed two MFMAs
-// each; at small chunks the longer per-workgroup stream of the gate/up pass
-// measured 10-17% faster (8-bit rows are half as long as bf16 ones, so one
+// Weight tiles per wavefront: 2 for 8-bit weights, 1 for bf16. Chunks of
+// more than 32 rows are bound by the activation fragment reads, which then
+// feed two MFMAs each; at small chunks the longer per-workgroup stream
+// measured 10-19% faster (8-bit rows are half as long as bf16 ones, so one
 // tile per wavefront leaves twice the workgroups, each with half the work).
+// The down projection's split count assumes this (256 output channels per
+// 8-bit workgroup).
 template <int MT, bool W8, bool GATEUP>
 constexpr int stream_wt() {
-  return (W8 && (GATEUP || MT >= 4)) ? 2 : 1;
+  return W8 ? 2 : 1;
 }
 
 // rows of one expert <= max_rows; chunks of 16*MT rows along grid z
