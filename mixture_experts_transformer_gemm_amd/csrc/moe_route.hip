@@ -71,6 +71,62 @@ __device__ __forceinline__ void raw8_f64(const Raw8<float>& r, double* o) {
   o[4] = r.b.x; o[5] = r.b.y; o[6] = r.b.z; o[7] = r.b.w;
 }
 
+// Softmax over the E logits of one token (lane e holds logit e; E <= 64),
+// then k rounds of shuffle arg-max over (p + bias desc, index asc); lane 0
+// writes the k routed slots (renormalised on request) and the ns shared ones.
+__device__ __forceinline__ void wave_route_token(double my_logit, int lane, int E, int k, int ns, int renorm,
+                                                 const float* __restrict__ bias, int64_t t,
+                                                 int32_t* __restrict__ idx, float* __restrict__ gate) {
+  const bool live = lane < E;
+  const double mx = wave_max_f64(live ? my_logit : -INFINITY);
+  const double ex = live ? exp(my_logit - mx) : 0.0;
+  const double z = wave_sum_f64(ex);
+  const double p = ex / z;
+  const double key = live ? p + (bias ? (double)bias[lane] : 0.0) : -INFINITY;
+  bool taken = false;
+  double gsel[8];
+  int isel[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    gsel[s] = 0.0;
+    isel[s] = 0;
+    if (s < k) {
+      // arg-max over the experts not yet taken; key (p + bias desc, index asc)
+      double kv = (live && !taken) ? key : -INFINITY;
+      int bi = lane;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const double ko = __shfl_xor(kv, off, 64);
+        const int io = __shfl_xor(bi, off, 64);
+        if (ko > kv || (ko == kv && io < bi)) {
+          kv = ko;
+          bi = io;
+        }
+      }
+      if (lane == bi) taken = true;
+      gsel[s] = __shfl(p, bi, 64);  // the gate is the probability itself
+      isel[s] = bi;
+    }
+  }
+  if (lane == 0) {
+    // Mixtral's renormalisation: the k gates over their sum (slot order)
+    double sum = 0.0;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) sum += gsel[s];
+    const int K = k + ns;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s < k) {
+        idx[t * K + s] = isel[s];
+        gate[t * K + s] = (float)(renorm ? gsel[s] / sum : gsel[s]);
+      }
+    for (int j = 0; j < ns; ++j) {
+      idx[t * K + k + j] = E + j;
+      gate[t * K + k + j] = 1.0f;
+    }
+  }
+}
+
 // One workgroup (4 wavefronts) per token, so the d-long dot products are
 // spread over 256 lanes and their loads are all in flight together. Each lane
 // accumulates 8 experts at a time over its 8-element chunks; the partials are
@@ -134,53 +190,76 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const XT* __restrict__
     if (wave == 0) {
       const bool live = lane < E;
       const double my_logit = live ? ((s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane])) : 0.0;
-      const double mx = wave_max_f64(live ? my_logit : -INFINITY);
-      const double ex = live ? exp(my_logit - mx) : 0.0;
-      const double z = wave_sum_f64(ex);
-      const double p = ex / z;
-      const double key = live ? p + (bias ? (double)bias[lane] : 0.0) : -INFINITY;
-      bool taken = false;
-      double gsel[8];
-      int isel[8];
+      wave_route_token(my_logit, lane, E, k, ns, renorm, bias, t, idx, gate);
+    }
+    __syncthreads();
+  }
+}
+
+// The same routing for 4 tokens per workgroup (larger batches): each lane
+// widens its router chunks once and uses them for the 4 tokens, so the
+// router weights are read from L2 once per 4 tokens; the per-lane chunk
+// order and the reductions are those of router_topk_kernel, so the logits
+// are bit-identical. Wavefront w then routes token w of the group.
+template <typename XT>
+__global__ __launch_bounds__(256) void router_topk4_kernel(const XT* __restrict__ x, const XT* __restrict__ wr,
+                                                           int64_t T, int d, int E, int k, int ns, int renorm,
+                                                           const float* __restrict__ bias,
+                                                           int32_t* __restrict__ idx, float* __restrict__ gate) {
+  constexpr int TPB = 4;
+  __shared__ double s_part[TPB][4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nchunk = d >> 3;
+  for (int64_t t0 = (int64_t)blockIdx.x * TPB; t0 < T; t0 += (int64_t)gridDim.x * TPB) {
+    const int nt = (int)min((int64_t)TPB, T - t0);
+    for (int e0 = 0; e0 < E; e0 += 8) {
+      double acc[TPB][8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        gsel[s] = 0.0;
-        isel[s] = 0;
-        if (s < k) {
-          // arg-max over the experts not yet taken; key (p + bias desc, index asc)
-          double kv = (live && !taken) ? key : -INFINITY;
-          int bi = lane;
+      for (int u = 0; u < TPB; ++u)
 #pragma unroll
-          for (int off = 32; off > 0; off >>= 1) {
-            const double ko = __shfl_xor(kv, off, 64);
-            const int io = __shfl_xor(bi, off, 64);
-            if (ko > kv || (ko == kv && io < bi)) {
-              kv = ko;
-              bi = io;
-            }
+        for (int j = 0; j < 8; ++j) acc[u][j] = 0.0;
+      for (int c = threadIdx.x; c < nchunk; c += 256) {
+        Raw8<XT> rx[TPB], rw[8];
+#pragma unroll
+        for (int u = 0; u < TPB; ++u)
+          if (u < nt) rx[u] = load_raw8(x + (t0 + u) * (int64_t)d + c * 8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (e0 + j < E) rw[j] = load_raw8(wr + (int64_t)(e0 + j) * d + c * 8);
+        double xv[TPB][8];
+#pragma unroll
+        for (int u = 0; u < TPB; ++u)
+          if (u < nt) raw8_f64(rx[u], xv[u]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (e0 + j < E) {
+            double wv[8];
+            raw8_f64(rw[j], wv);
+#pragma unroll
+            for (int u = 0; u < TPB; ++u)
+              if (u < nt) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[u][j] = fma(xv[u][q], wv[q], acc[u][j]);
+              }
           }
-          if (lane == bi) taken = true;
-          gsel[s] = __shfl(p, bi, 64);  // the gate is the probability itself
-          isel[s] = bi;
         }
       }
-      if (lane == 0) {
-        // Mixtral's renormalisation: the k gates over their sum (slot order)
-        double sum = 0.0;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) sum += gsel[s];
-        const int K = k + ns;
+      for (int u = 0; u < TPB; ++u)
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-          if (s < k) {
-            idx[t * K + s] = isel[s];
-            gate[t * K + s] = (float)(renorm ? gsel[s] / sum : gsel[s]);
-          }
-        for (int j = 0; j < ns; ++j) {
-          idx[t * K + k + j] = E + j;
-          gate[t * K + k + j] = 1.0f;
+        for (int j = 0; j < 8; ++j) {
+          const double sm = wave_sum_f64(acc[u][j]);
+          if (lane == 0 && e0 + j < E) s_part[u][wave][e0 + j] = sm;
         }
-      }
+    }
+    __syncthreads();
+    if (wave < nt) {
+      const bool live = lane < E;
+      const double my_logit =
+          live ? ((s_part[wave][0][lane] + s_part[wave][1][lane]) + (s_part[wave][2][lane] + s_part[wave][3][lane]))
+               : 0.0;
+      wave_route_token(my_logit, lane, E, k, ns, renorm, bias, t0 + wave, idx, gate);
     }
     __syncthreads();
   }
@@ -188,6 +267,17 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const XT* __restrict__
 
 hipError_t launch_router(int act_f32, const void* x, const void* router_w, int64_t T, int d, int E, int k, int ns,
                          int renorm, const float* bias, int32_t* idx, float* gate, hipStream_t stream) {
+  if (T >= 256) {  // 4 tokens per workgroup
+    int64_t blocks = (T + 3) / 4;
+    if (blocks > 16384) blocks = 16384;
+    if (act_f32)
+      hipLaunchKernelGGL(router_topk4_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                         (const float*)x, (const float*)router_w, T, d, E, k, ns, renorm, bias, idx, gate);
+    else
+      hipLaunchKernelGGL(router_topk4_kernel<bf16_bits>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                         (const bf16_bits*)x, (const bf16_bits*)router_w, T, d, E, k, ns, renorm, bias, idx, gate);
+    return hipGetLastError();
+  }
   int64_t blocks = T;
   if (blocks > 16384) blocks = 16384;
   if (blocks < 1) blocks = 1;

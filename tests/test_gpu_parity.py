@@ -64,7 +64,7 @@ def test_tiny_f32_workload():
     _full_check(w)
 
 
-@pytest.mark.parametrize("T,d,f", [(1, 8, 4), (7, 24, 20), (33, 64, 96)])
+@pytest.mark.parametrize("T,d,f", [(1, 8, 4), (7, 24, 20), (33, 64, 96), (301, 64, 96)])
 def test_f32_layer_odd_shapes(T, d, f):
     w = synthetic.make("tiny_f32", T=T, d=d, f=f, seed=T)
     _full_check(w)
@@ -216,3 +216,25 @@ def test_permutation_many_blocks(E, k, cf):
     ref = oracle.forward_given_routing(w.x, w.w_gate, w.w_up, w.w_down, idx,
                                        np.where(pos >= 0, gate, 0.0).astype(np.float64), tokens=toks)
     assert normwise_err(got[toks], ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "i8"])
+def test_tile_boundaries_and_empty_experts(w_dtype):
+    # 1,100 tokens at top-2 average 275 rows per expert, so bf16 weights run 320-row tiles (8-bit: 128-row):
+    # segments of 0, 1, 319, 320, 321, 640, 599 and 0 rows put tile edges on both sides of every boundary
+    # and leave the first and last experts empty (tile table entries must skip them)
+    T, E, k = 1100, 8, 2
+    sizes = [0, 1, 319, 320, 321, 640, 599, 0]
+    labels = np.repeat(np.arange(E, dtype=np.int32), sizes)            # sorted by expert, 2T long
+    idx = np.stack([labels[:T], labels[T:]], axis=1)                   # runs < T long: distinct per token
+    assert np.all(idx[:, 0] != idx[:, 1])
+    rng = np.random.default_rng(11)
+    idx = idx[rng.permutation(T)]
+    gate = rng.random((T, k)).astype(np.float32)
+    w = synthetic.make("decode", T=T, d=256, f=512, E=E, k=k, seed=12, w_dtype=w_dtype)
+    got, dbg = run_layer(w, torch, route_idx=idx, route_gate=gate)
+    check_permutation(idx, dbg, E)
+    assert list(dbg["counts"]) == sizes
+    ref = oracle.forward_given_routing(w.x, w.w_gate, w.w_up, w.w_down, idx, gate.astype(np.float64),
+                                       scales=w.scales)
+    assert normwise_err(got, ref) <= TOL["i8" if w_dtype == "i8" else "bf16"]

@@ -202,7 +202,7 @@ def test_capacity_skew_full_sampled():
 # ---------------------------------------------------------------- fine-grained: many experts, bias, shared experts
 @pytest.mark.parametrize("T,E", [(1, 256), (8, 256), (64, 256), (300, 256), (1000, 256), (40, 72), (200, 100)])
 def test_fine_grained_bf16(T, E):
-    # E > 64: the split-K fp64 router GEMM + one-wavefront top-k; top-8, one shared expert, selection bias
+    # E > 64: the split-K fp64 MFMA router GEMM + per-token top-k; top-8, one shared expert, selection bias
     w = synthetic.make("dsv3_decode", T=T, d=256, f=256, E=E, seed=400 + T)
     got, dbg, _ = _check(w, label="fine-grained")
     assert (dbg["idx"][:, 8] == E).all() and (dbg["gate"][:, 8] == 1.0).all()
