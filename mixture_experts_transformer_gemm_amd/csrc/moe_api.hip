@@ -98,12 +98,12 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
   if (E > kFusedRouterE) {
     // many-expert router: its (64 tokens x 256 experts) tiles split the
     // reduction into whole 64-wide chunks until about 512 workgroups (two
-    // per CU) run, keeping at least 4 chunks per split so that the top-k
+    // per CU) run, keeping at least 2 chunks per split so that the top-k
     // kernel sums few partials
     const int64_t rtiles = ((T + 63) / 64) * ((E + 255) / 256);
     const int nchunk = (int)(d / 64);
     int s = 1;
-    for (int c = 2; c <= nchunk / 4; ++c)
+    for (int c = 2; c <= nchunk / 2; ++c)
       if (nchunk % c == 0 && rtiles * c <= 512) s = c;
     p.rsplits = s;
   }

@@ -294,9 +294,9 @@ hipError_t launch_router(int act_f32, const void* x, const void* router_w, int64
 // Fine-grained layers route over hundreds of experts (256 in DeepSeek-V3,
 // book ch. 10, section 10.1 table). The logits become a [T][E] GEMM in two
 // kernels: router_mfma_kernel forms split-K partial logits in fp64 (each
-// bf16 product is exact in fp64), router_topk_block_kernel sums the
-// partials in split order and runs softmax and top-k with one workgroup per
-// token.
+// bf16 product is exact in fp64); router_topk_wave_kernel (up to 8 splits,
+// one wavefront per token) or router_topk_block_kernel (one workgroup per
+// token) sums the partials in split order and runs softmax and top-k.
 
 // Workgroup tile: 64 tokens x 256 experts (wavefront w: experts 64 w ..
 // 64 w + 63), reduction chunks of 64 staged as bf16 in LDS (rows padded to 72
@@ -419,106 +419,153 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_bits* __res
     }
 }
 
-// One workgroup per token, thread e holding expert e (E <= 256): the split
-// partials of its logit summed in split order, softmax with workgroup
-// reductions in fixed order, then k rounds of arg-max over (p + b, index).
-__global__ __launch_bounds__(256) void router_topk_block_kernel(const double* __restrict__ P, int S, int64_t T, int E,
-                                                                int k, int ns, int renorm,
-                                                                const float* __restrict__ bias,
-                                                                int32_t* __restrict__ idx, float* __restrict__ gate) {
-  __shared__ double s_red[4];
-  __shared__ double s_key[4], s_p[4];
-  __shared__ int s_idx[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = k + ns;
-  const bool live = tid < E;
+// Softmax and the k rounds of arg-max over (p + b desc, index asc) for one
+// token in one wavefront: lane l holds the logits of experts l, l + 64,
+// l + 128, l + 192 (-inf past E). No workgroup barriers. E <= 256.
+__device__ __forceinline__ void wave_route_many(const double (&lg)[4], int lane, int E, int k, int ns, int renorm,
+                                                const float* __restrict__ bias, int64_t t,
+                                                int32_t* __restrict__ idx, float* __restrict__ gate) {
+  double p[4], key[4];
+  bool live[4], taken[4];
+  double m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    live[j] = lane + 64 * j < E;
+    taken[j] = false;
+    m = fmax(m, lg[j]);
+  }
+  m = wave_max_f64(m);
+  double z = 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    p[j] = live[j] ? exp(lg[j] - m) : 0.0;
+    z += p[j];
+  }
+  z = wave_sum_f64(z);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    p[j] /= z;
+    key[j] = live[j] ? p[j] + (bias ? (double)bias[lane + 64 * j] : 0.0) : -INFINITY;
+  }
+  double gsel[8];
+  int isel[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    gsel[r] = 0.0;
+    isel[r] = 0;
+    if (r < k) {
+      // this lane's best untaken expert (ascending index breaks ties), then across lanes
+      double kv = -INFINITY, pv = 0.0;
+      int bi = 1 << 30;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (live[j] && !taken[j] && key[j] > kv) {
+          kv = key[j];
+          pv = p[j];
+          bi = lane + 64 * j;
+        }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const double ko = __shfl_xor(kv, off, 64);
+        const double po = __shfl_xor(pv, off, 64);
+        const int io = __shfl_xor(bi, off, 64);
+        if (ko > kv || (ko == kv && io < bi)) {
+          kv = ko;
+          pv = po;
+          bi = io;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (bi == lane + 64 * j) taken[j] = true;
+      gsel[r] = pv;
+      isel[r] = bi < E ? bi : -1;  // -1 (dropped) only when no key compares, i.e. NaN logits
+    }
+  }
+  if (lane == 0) {
+    double sum = 0.0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) sum += gsel[r];
+    const int K = k + ns;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      if (r < k) {
+        idx[t * K + r] = isel[r];
+        gate[t * K + r] = (float)(renorm ? gsel[r] / sum : gsel[r]);
+      }
+    for (int jj = 0; jj < ns; ++jj) {
+      idx[t * K + k + jj] = E + jj;
+      gate[t * K + k + jj] = 1.0f;
+    }
+  }
+}
+
+// Few split partials (S <= 8): one wavefront per token, lane l summing the
+// partials of its four experts in split order, then wave_route_many.
+__global__ __launch_bounds__(256) void router_topk_wave_kernel(const double* __restrict__ P, int S, int64_t T, int E,
+                                                               int k, int ns, int renorm,
+                                                               const float* __restrict__ bias,
+                                                               int32_t* __restrict__ idx, float* __restrict__ gate) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t < T; t += (int64_t)gridDim.x * 4) {
+    const double* pt = P + t * E;
+    const int64_t stride = T * E;
+    double v[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) v[j][s] = (s < S && lane + 64 * j < E) ? pt[s * stride + lane + 64 * j] : 0.0;
+    double lg[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lg[j] = 0.0;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        if (s < S) lg[j] += v[j][s];
+      if (lane + 64 * j >= E) lg[j] = -INFINITY;
+    }
+    wave_route_many(lg, lane, E, k, ns, renorm, bias, t, idx, gate);
+  }
+}
+
+// More partials: one workgroup of 1024 threads per token. Thread (g, e)
+// (g = tid / 256) sums the partials [g S / 4, (g + 1) S / 4) of logit e in
+// split order, eight loads at a time; the four quarter sums are added in
+// fixed order and wavefront 0 routes the token.
+__global__ __launch_bounds__(1024) void router_topk_block_kernel(const double* __restrict__ P, int S, int64_t T, int E,
+                                                                 int k, int ns, int renorm,
+                                                                 const float* __restrict__ bias,
+                                                                 int32_t* __restrict__ idx, float* __restrict__ gate) {
+  __shared__ double s_part[4][256];
+  const int tid = threadIdx.x, lane = tid & 63, g = tid >> 8, e = tid & 255;
+  const int s0 = g * S / 4, s1 = (g + 1) * S / 4;
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
-    double lg = 0.0;
-    if (live) {
-      // eight partials loaded at a time, added in split order
-      const double* pe = P + t * E + tid;
+    if (e < E) {
+      const double* pe = P + t * E + e;
       const int64_t stride = T * E;
-      int s = 0;
-      for (; s + 8 <= S; s += 8) {
+      double sum = 0.0;
+      int s = s0;
+      for (; s + 8 <= s1; s += 8) {
         double v[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) v[q] = pe[(int64_t)(s + q) * stride];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) lg += v[q];
+        for (int q = 0; q < 8; ++q) sum += v[q];
       }
-      for (; s < S; ++s) lg += pe[(int64_t)s * stride];
+      for (; s < s1; ++s) sum += pe[(int64_t)s * stride];
+      s_part[g][e] = sum;
     }
-    double m = wave_max_f64(live ? lg : -INFINITY);
-    if (lane == 0) s_red[wave] = m;
     __syncthreads();
-    m = fmax(fmax(s_red[0], s_red[1]), fmax(s_red[2], s_red[3]));
-    __syncthreads();
-    const double ex = live ? exp(lg - m) : 0.0;
-    double z = wave_sum_f64(ex);
-    if (lane == 0) s_red[wave] = z;
-    __syncthreads();
-    z = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
-    __syncthreads();
-    const double p = ex / z;
-    const double key = live ? p + (bias ? (double)bias[tid] : 0.0) : -INFINITY;
-    bool taken = false;
-    double gsel[8];
-    int isel[8];
+    if (tid < 64) {
+      double lg[4];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      gsel[s] = 0.0;
-      isel[s] = 0;
-      if (s < k) {
-        double kv = (live && !taken) ? key : -INFINITY, pv = p;
-        int bi = tid;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-          const double ko = __shfl_xor(kv, off, 64);
-          const double po = __shfl_xor(pv, off, 64);
-          const int io = __shfl_xor(bi, off, 64);
-          if (ko > kv || (ko == kv && io < bi)) {
-            kv = ko;
-            pv = po;
-            bi = io;
-          }
-        }
-        if (lane == 0) {
-          s_key[wave] = kv;
-          s_p[wave] = pv;
-          s_idx[wave] = bi;
-        }
-        __syncthreads();
-        kv = s_key[0];
-        pv = s_p[0];
-        bi = s_idx[0];
-#pragma unroll
-        for (int w = 1; w < 4; ++w)
-          if (s_key[w] > kv || (s_key[w] == kv && s_idx[w] < bi)) {
-            kv = s_key[w];
-            pv = s_p[w];
-            bi = s_idx[w];
-          }
-        __syncthreads();
-        if (tid == bi) taken = true;
-        gsel[s] = pv;
-        isel[s] = bi;
+      for (int j = 0; j < 4; ++j) {
+        const int ej = lane + 64 * j;
+        lg[j] = ej < E ? (s_part[0][ej] + s_part[1][ej]) + (s_part[2][ej] + s_part[3][ej]) : -INFINITY;
       }
+      wave_route_many(lg, lane, E, k, ns, renorm, bias, t, idx, gate);
     }
-    if (tid == 0) {
-      double sum = 0.0;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) sum += gsel[s];
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        if (s < k) {
-          idx[t * K + s] = isel[s];
-          gate[t * K + s] = (float)(renorm ? gsel[s] / sum : gsel[s]);
-        }
-      for (int j = 0; j < ns; ++j) {
-        idx[t * K + k + j] = E + j;
-        gate[t * K + k + j] = 1.0f;
-      }
-    }
+    __syncthreads();
   }
 }
 
@@ -529,9 +576,16 @@ hipError_t launch_router_many(const bf16_bits* x, const bf16_bits* router_w, int
   hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(256), 0, stream, x, router_w, T, d, E, P);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (splits <= 8) {
+    int64_t blocks = (T + 3) / 4;
+    if (blocks > 16384) blocks = 16384;
+    hipLaunchKernelGGL(router_topk_wave_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, P, splits, T, E, k, ns,
+                       renorm, bias, idx, gate);
+    return hipGetLastError();
+  }
   int64_t blocks = T < 16384 ? T : 16384;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(router_topk_block_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, P, splits, T, E, k, ns,
+  hipLaunchKernelGGL(router_topk_block_kernel, dim3((unsigned)blocks), dim3(1024), 0, stream, P, splits, T, E, k, ns,
                      renorm, bias, idx, gate);
   return hipGetLastError();
 }
