@@ -1003,21 +1003,35 @@ hipError_t launch_tile_table(const int32_t* counts, int E, int bm, int32_t* tile
 __device__ __forceinline__ float4 gated_sum4(const float* __restrict__ Y, int S, int64_t split_stride,
                                              const int32_t* __restrict__ pos, const float* __restrict__ gate,
                                              int64_t t, int d, int k, int c) {
+  // every slot's row and first partial are loaded before any is added (k <= 12)
+  int row[kPermMaxK];
+  float g[kPermMaxK];
+  float4 y[kPermMaxK];
+#pragma unroll
+  for (int s = 0; s < kPermMaxK; ++s) {
+    row[s] = -1;
+    if (s < k) {
+      row[s] = pos[t * k + s];
+      g[s] = gate[t * k + s];
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < kPermMaxK; ++s)
+    if (s < k && row[s] >= 0) y[s] = *reinterpret_cast<const float4*>(Y + (int64_t)row[s] * d + c);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < k; ++s) {
-    const int row = pos[t * k + s];
-    if (row < 0) continue;
-    const float g = gate[t * k + s];
-    const float* yr = Y + (int64_t)row * d + c;
-    float4 y = *reinterpret_cast<const float4*>(yr);
+#pragma unroll
+  for (int s = 0; s < kPermMaxK; ++s) {
+    if (s >= k || row[s] < 0) continue;
+    float4 v = y[s];
+    const float* yr = Y + (int64_t)row[s] * d + c;
     for (int p = 1; p < S; ++p) {
       const float4 q = *reinterpret_cast<const float4*>(yr + p * split_stride);
-      y.x += q.x; y.y += q.y; y.z += q.z; y.w += q.w;
+      v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
     }
-    acc.x += g * y.x;
-    acc.y += g * y.y;
-    acc.z += g * y.z;
-    acc.w += g * y.w;
+    acc.x += g[s] * v.x;
+    acc.y += g[s] * v.y;
+    acc.z += g[s] * v.z;
+    acc.w += g[s] * v.w;
   }
   return acc;
 }
