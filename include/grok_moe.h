@@ -44,8 +44,9 @@
  *    shared experts; bf16 and 8-bit weights need d % 256 == 0 and
  *    f % 256 == 0; fp32 needs d % 8 == 0 and f % 4 == 0; T <= 2^20.
  *  - Pointers must be 16-byte aligned (GROK_MOE_EALIGN otherwise).
- *  - Thread-safe: no global mutable state. Concurrent calls on different
- *    streams need separate workspaces (the plain forms allocate their own).
+ *  - Thread-safe: the only global state is each kernel's LDS limit, set
+ *    once per device on first use. Concurrent calls on different streams
+ *    need separate workspaces (the plain forms allocate their own).
  */
 #ifndef GROK_MOE_H
 #define GROK_MOE_H

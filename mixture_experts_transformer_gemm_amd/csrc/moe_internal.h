@@ -5,7 +5,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace gmoe {
+
+// Raises kernel `fn`'s dynamic LDS limit to `bytes` on the current device,
+// once per device (the attribute belongs to the device's copy of the
+// kernel); `done` is the caller's per-kernel bit set of devices 0..63.
+// Thread-safe: a race sets the attribute twice, which is harmless.
+inline hipError_t set_lds_limit(const void* fn, int bytes, std::atomic<unsigned long long>& done) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const unsigned long long bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0ull;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (err == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+  return err;
+}
 
 // Raw bf16 values travel as uint16_t bit patterns.
 typedef uint16_t bf16_bits;

@@ -331,9 +331,9 @@ static hipError_t stream_launch(unsigned gz, unsigned gy, hipStream_t st, const 
                                 const void* w0, const void* w1, const float* scales, int64_t T, int K, int N, int E,
                                 int64_t rows_cap, int act, void* out) {
   constexpr int lds = BsCfg<MT, W8, WT>::kLdsBytes;
-  static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&stream_kernel<GATEUP, MT, W8, WT>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  static std::atomic<unsigned long long> lds_set{0};
+  const hipError_t attr =
+      set_lds_limit(reinterpret_cast<const void*>(&stream_kernel<GATEUP, MT, W8, WT>), lds, lds_set);
   if (attr != hipSuccess) return attr;
   // one workgroup per (expert, 8 wavefronts x channels per wavefront)
   const unsigned gx = (unsigned)E * (unsigned)(N / (kBW * (GATEUP ? 8 : 16) * WT));

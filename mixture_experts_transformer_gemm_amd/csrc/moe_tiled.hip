@@ -472,9 +472,9 @@ static hipError_t launch_dma(hipStream_t st, const bf16_bits* A, RouteView rv, c
                              int splits, int act, void* out) {
   using P = DmaChoice<BM, W8>;
   constexpr int lds = DmaCfg<BM, P::NW, P::NS, W8>::kLdsBytes;
-  static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&dma_kernel<BM, GATEUP, P::NW, P::NS, W8>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  static std::atomic<unsigned long long> lds_set{0};
+  const hipError_t attr =
+      set_lds_limit(reinterpret_cast<const void*>(&dma_kernel<BM, GATEUP, P::NW, P::NS, W8>), lds, lds_set);
   if (attr != hipSuccess) return attr;
   const dim3 grid(tiled_blocks(BM, rows_cap, E, N / (GATEUP ? TBN / 2 : TBN)), (unsigned)splits);
   hipLaunchKernelGGL((dma_kernel<BM, GATEUP, P::NW, P::NS, W8>), grid, dim3(P::NW * 64), lds, st, A, rv, w0, w1,
