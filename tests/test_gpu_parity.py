@@ -238,3 +238,27 @@ def test_tile_boundaries_and_empty_experts(w_dtype):
     ref = oracle.forward_given_routing(w.x, w.w_gate, w.w_up, w.w_down, idx, gate.astype(np.float64),
                                        scales=w.scales)
     assert normwise_err(got, ref) <= TOL["i8" if w_dtype == "i8" else "bf16"]
+
+
+@pytest.mark.parametrize("E,k,ns", [(8, 2, 0), (72, 8, 1)])
+def test_non_finite_tokens_stay_local(E, k, ns):
+    # inputs outside the contract (NaN / Inf in some tokens) must not crash, hang or leak into other
+    # tokens: every GEMM row, router row and combine row is computed from its own token only
+    T = 100
+    w = synthetic.make("dsv3_decode" if ns else "decode", T=T, d=256, f=256, E=E, k=k, seed=21)
+    bad = [5, 17, 63]
+    nan_bits, inf_bits = np.uint16(0x7FC0), np.uint16(0x7F80)
+    w.x = w.x.copy()
+    w.x[5, :] = nan_bits
+    w.x[17, 3] = inf_bits
+    w.x[63, 200] = nan_bits
+    got, dbg = run_layer(w, torch)
+    clean = np.array([t for t in range(T) if t not in bad])
+    ref = oracle.layer(w.x[clean], w.router_w, w.w_gate, w.w_up, w.w_down, w.k,
+                       activation=oracle.SILU if w.activation == "silu" else oracle.GELU,
+                       renormalize=w.renormalize, n_shared=w.n_shared, router_bias=w.router_bias)
+    np.testing.assert_array_equal(dbg["idx"][clean], ref["idx"])
+    assert np.all(np.isfinite(got[clean]))
+    assert normwise_err(got[clean], ref["out"]) <= TOL["bf16"]
+    # the routing of the bad tokens is valid or dropped (-1), never outside [0, E + ns)
+    assert np.all((dbg["idx"][bad] >= -1) & (dbg["idx"][bad] < E + ns))
