@@ -11,11 +11,12 @@
 // wavefronts, 256 or 320 with 8). For the gate/up pass the 256 weight rows
 // are 128 gate channels and the same 128 up channels, so act(gate) * up is
 // formed in registers. With two wavefront rows, row subtile q (32 rows) goes
-// to wavefront row q mod 2, so a partly filled tile keeps both busy. Products use v_mfma_f32_32x32x16_bf16 with the weight fragment
-// as the "A" operand (32 channels) and the activation fragment as "B" (32
-// rows): lane l supplies row (l mod 32) and the 8 reduction values of group
-// l / 32; result register v of lane l is C[8 (v / 4) + 4 (l / 32) + (v mod
-// 4)][l mod 32], so each lane owns runs of 4 consecutive channels of one row.
+// to wavefront row q mod 2, so a partly filled tile keeps both busy.
+// Products use v_mfma_f32_32x32x16_bf16 with the weight fragment as the "A"
+// operand (32 channels) and the activation fragment as "B" (32 rows): lane l
+// supplies row (l mod 32) and the 8 reduction values of group l / 32; result
+// register v of lane l is C[8 (v / 4) + 4 (l / 32) + (v mod 4)][l mod 32], so
+// each lane owns runs of 4 consecutive channels of one row.
 //
 // Both operands reach LDS by global_load_lds_dwordx4 (no staging registers):
 // stages of 64 reduction values, as many stages as fit in 144 KB (2 for the
