@@ -39,7 +39,7 @@ def _full_check(w, scales=None, expect_exact_routing=True):
     return got, dbg, err
 
 
-@pytest.mark.parametrize("T", [1, 5, 8, 16, 37, 63, 64, 65, 100, 128, 129, 257, 300, 777, 2049])
+@pytest.mark.parametrize("T", [1, 5, 8, 16, 24, 32, 37, 63, 64, 65, 100, 128, 129, 257, 300, 777, 2049])
 def test_bf16_layer_small(T):
     w = synthetic.make("decode", T=T, d=256, f=512, seed=T)
     _full_check(w)
@@ -51,7 +51,7 @@ def test_bf16_layer_other_shapes(T, d, f):
     _full_check(w)
 
 
-@pytest.mark.parametrize("T", [3, 40, 128, 200, 513, 1600])
+@pytest.mark.parametrize("T", [3, 24, 40, 128, 200, 513, 1600])
 def test_int8_layer_small_random_scales(T):
     # distinct per-channel scales pin which output channel each scale belongs to
     w = synthetic.make("int8", T=T, d=256, f=512, seed=T)
