@@ -70,7 +70,8 @@ def test_f32_layer_odd_shapes(T, d, f):
     _full_check(w)
 
 
-@pytest.mark.parametrize("E,k,T", [(1, 1, 20), (4, 1, 50), (2, 2, 9), (16, 4, 60), (64, 8, 50), (16, 4, 260)])
+@pytest.mark.parametrize("E,k,T", [(1, 1, 20), (4, 1, 50), (2, 2, 9), (16, 4, 60), (64, 8, 50), (16, 4, 260),
+                                   (1, 1, 700), (2, 1, 333), (64, 8, 300), (32, 2, 5000)])
 def test_expert_and_k_variants(E, k, T):
     w = synthetic.make("decode", T=T, d=256, f=256, E=E, k=k, seed=E * 10 + k)
     _full_check(w)
