@@ -260,12 +260,15 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
       }
     }
   };
-  // MV: tiles that get MFMAs (the chunk's rows rounded up to MT/2, 3MT/4
-  // (128-row chunks only) or MT tiles; rows past the segment's end repeat
-  // its last row)
+  // MV: tiles that get MFMAs (the chunk's rows rounded up to MT/4 (chunks
+  // of 64 rows or more), MT/2, 3MT/4 (128-row chunks only) or MT tiles; rows
+  // past the segment's end repeat its last row)
   constexpr int kHalf = MT > 1 ? MT / 2 : 1;
+  constexpr int kQuarter = MT >= 4 ? MT / 4 : kHalf;
   auto run_naw = [&](auto naw_tag) __attribute__((always_inline)) {
-    if (mv <= kHalf)
+    if (kQuarter < kHalf && mv <= kQuarter)
+      run(naw_tag, std::integral_constant<int, kQuarter>{});
+    else if (mv <= kHalf)
       run(naw_tag, std::integral_constant<int, kHalf>{});
     else if (MT == 8 && mv <= 6)  // 128-row chunks also stop at 96 rows
       run(naw_tag, std::integral_constant<int, (MT == 8 ? 6 : MT)>{});
