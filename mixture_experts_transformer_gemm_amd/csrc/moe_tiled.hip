@@ -457,14 +457,17 @@ static unsigned tiled_blocks(int bm, int64_t rows_cap, int E, int nN) {
   return (unsigned)(((mt_ub * nN) + 7) / 8 * 8);
 }
 
-// Pipeline shape per tile height: 256-row tiles run 8 wavefronts (two per
-// SIMD, so one's MFMAs cover the other's waits); as many LDS stages as fit
-// in 144 KB, at most 6.
+// Pipeline shape per tile height: 256- and 320-row tiles run 8 wavefronts
+// (two per SIMD, so one's MFMAs cover the other's waits); as many LDS stages
+// as fit in 144 KB, at most 6, except for 8-bit weights, whose smaller
+// stages measured faster less deep: 2 stages for 256-row tiles (3.5% faster
+// than 3 at 8,192 tokens), 3 for 128-row tiles (4% faster than 4).
 template <int BM, bool W8>
 struct DmaChoice {
   static constexpr int NW = BM >= 256 ? 8 : 4;
   static constexpr int kStage = DmaCfg<BM, NW, 2, W8>::kStageBytes;
-  static constexpr int NS = 147456 / kStage < 6 ? 147456 / kStage : 6;
+  static constexpr int kFit = 147456 / kStage < 6 ? 147456 / kStage : 6;
+  static constexpr int NS = !W8 ? kFit : (BM >= 256 ? 2 : (BM == 128 && kFit > 3 ? 3 : kFit));
 };
 
 template <int BM, bool GATEUP, bool W8>
