@@ -46,9 +46,15 @@ def test_workspace_bytes():
     # decode shape: idx/gate/perm/pos + H [16, f] bf16 + split-K Y partials
     ws = gm.grok_moe_workspace_bytes(8, 6144, 32768, 8, 2)
     assert ws >= 16 * 32768 * 2 + 16 * 6144 * 4
-    # prefill: H [16384, 32768] bf16 dominates; Y [16384, 6144] fp32; u [8192, 6144] bf16 for the sandwich norms
+    # prefill: H [16384, 32768] bf16 dominates; Y [2][16384, 6144] fp32 (its 1,344 down tiles leave the
+    # last of 256 workgroup rounds a quarter full, so the reduction runs in two splits); u [8192, 6144]
+    # bf16 for the sandwich norms
     ws = gm.grok_moe_workspace_bytes(8192, 6144, 32768, 8, 2)
-    assert 16384 * 32768 * 2 <= ws < 16384 * 32768 * 2 + 16384 * 6144 * 4 + 8192 * 6144 * 2 + (1 << 20)
+    assert 16384 * 32768 * 2 + 2 * 16384 * 6144 * 4 <= ws
+    assert ws < 16384 * 32768 * 2 + 2 * 16384 * 6144 * 4 + 8192 * 6144 * 2 + (1 << 20)
+    # 16,384 tokens: 2,496 down tiles (9.75 rounds), one split
+    ws = gm.grok_moe_workspace_bytes(16384, 6144, 32768, 8, 2)
+    assert ws < 32768 * 32768 * 2 + 32768 * 6144 * 4 + 16384 * 6144 * 2 + (1 << 20)
     assert gm.grok_moe_workspace_bytes(0, 6144, 32768, 8, 2) > 0
     # invalid / unsupported shapes report 0
     assert gm.grok_moe_workspace_bytes(8, 6144, 32768, 8, 9) == 0          # k > E
