@@ -151,22 +151,25 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const XT* __restrict__
       double acc[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] = 0.0;
-      // two chunks per trip, all their loads issued before the first FMA
-      for (int c = threadIdx.x; c < nchunk; c += 512) {
-        const bool has2 = c + 256 < nchunk;
-        Raw8<XT> rx[2], rw[2][8];
-        rx[0] = load_raw8(xr + c * 8);
-        if (has2) rx[1] = load_raw8(xr + (c + 256) * 8);
+      // U chunks per trip (c0, c0 + 256, ...; one trip covers d = 8192 bf16
+      // or 4096 fp32), all their loads issued before the first FMA; the FMAs
+      // then run in ascending chunk order, the order of router_topk4_kernel
+      constexpr int U = sizeof(XT) == 2 ? 4 : 2;
+      for (int c0 = threadIdx.x; c0 < nchunk; c0 += 256 * U) {
+        Raw8<XT> rx[U], rw[U][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (e0 + j < E) {
-            rw[0][j] = load_raw8(wr + (int64_t)(e0 + j) * d + c * 8);
-            if (has2) rw[1][j] = load_raw8(wr + (int64_t)(e0 + j) * d + (c + 256) * 8);
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + 256 * u;
+          if (c < nchunk) {
+            rx[u] = load_raw8(xr + c * 8);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (e0 + j < E) rw[u][j] = load_raw8(wr + (int64_t)(e0 + j) * d + c * 8);
           }
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          if (u == 1 && !has2) break;
+        for (int u = 0; u < U; ++u) {
+          if (c0 + 256 * u >= nchunk) break;
           double xv[8];
           raw8_f64(rx[u], xv);
 #pragma unroll
