@@ -55,6 +55,9 @@ def test_workspace_bytes():
     # 16,384 tokens: 2,496 down tiles (9.75 rounds), one split
     ws = gm.grok_moe_workspace_bytes(16384, 6144, 32768, 8, 2)
     assert ws < 32768 * 32768 * 2 + 32768 * 6144 * 4 + 16384 * 6144 * 2 + (1 << 20)
+    # 32,768 tokens: 4,992 down tiles (19.5 rounds), two splits
+    ws = gm.grok_moe_workspace_bytes(32768, 6144, 32768, 8, 2)
+    assert ws >= 65536 * 32768 * 2 + 2 * 65536 * 6144 * 4
     assert gm.grok_moe_workspace_bytes(0, 6144, 32768, 8, 2) > 0
     # invalid / unsupported shapes report 0
     assert gm.grok_moe_workspace_bytes(8, 6144, 32768, 8, 9) == 0          # k > E

@@ -89,3 +89,11 @@ def test_prefill_full():
     pairs = {tuple(sorted(p)) for p in dbg["idx"].tolist()}
     assert len(pairs) == 28
     assert counts.sum() == 2 * 8192
+
+
+def test_prefill_T32768_full():
+    # four times the prefill batch: 65,536 rows, 26 row tiles of 320 per expert (53,248 gate/up
+    # workgroups), and 4,992 down tiles (19.5 rounds of 256 CUs), so the down reduction runs in two
+    # splits; every token's routing and the permutation are checked, outputs on a sample
+    dbg, counts = _run_and_check("prefill", n_random=4, T=32768)
+    assert counts.sum() == 2 * 32768
