@@ -101,7 +101,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
     const int64_t exp_tiles =
         ((int64_t)E * ((T * k / E + p.bm - 1) / p.bm) + (int64_t)ns * ((T + p.bm - 1) / p.bm)) * (d / 256);
     const int64_t last = exp_tiles % 256;
-    if (s == 1 && last > 0 && last <= 128 && (f / 4) % 64 == 0) s = 2;
+    if (s == 1 && last > 0 && last <= 128 && (f / 2) % 64 == 0) s = 2;
     p.splits = s;
   }
   if (E > kFusedRouterE) {
