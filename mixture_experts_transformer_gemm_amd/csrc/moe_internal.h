@@ -115,10 +115,12 @@ hipError_t launch_combine_sandwich(int out_f32, const float* Y, int S, int64_t r
 
 // Weight-streaming path: bf16 weights with every expert segment <= max_rows
 // <= 64 rows, or 8-bit weights (w8, scales) with segments processed in
-// chunks of up to 128 rows.
-hipError_t launch_stream_gateup(int w8, int max_rows, const bf16_bits* x, RouteView rv, const void* wg,
-                                const void* wu, const float* scales, int64_t T, int d, int f, int E, int act,
-                                bf16_bits* H, hipStream_t stream);
+// chunks of up to 128 rows. splits > 1: the gate/up reduction runs in that
+// many slices whose fp32 sums go to G [splits][rows_cap][2f] (gate channels,
+// then up channels), and a second kernel forms H from them.
+hipError_t launch_stream_gateup(int w8, int max_rows, int splits, const bf16_bits* x, RouteView rv, const void* wg,
+                                const void* wu, const float* scales, int64_t T, int64_t rows_cap, int d, int f, int E,
+                                int act, bf16_bits* H, float* G, hipStream_t stream);
 hipError_t launch_stream_down(int w8, int max_rows, int splits, const bf16_bits* H, RouteView rv, const void* wd,
                               const float* scales, int64_t rows_cap, int d, int f, int E, float* Y,
                               hipStream_t stream);

@@ -295,7 +295,19 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
     for (int j = 0; j < MT; ++j) {
       if (j < mv) {
         const int m = 16 * j + r16;  // activation row (within the chunk) of this lane's results
-        if (GATEUP) {
+        if (GATEUP && S > 1) {
+          // split sp's sums: lanes with g < 2 hold gate channels cw + 4g.., the
+          // others the same up channels; G row = [gate 0..N) [up 0..N)
+          if (m < rows) {
+            const int up = g >> 1, ch = cw + 4 * (g & 1);
+            float y[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              y[v] = acc[w][j][v] * (W8 ? scales[(int64_t)up * E * N + (int64_t)e * N + ch + v] : 1.f);
+            float* Gs = (float*)out + ((int64_t)sp * rows_cap + m0 + m) * (2 * (int64_t)N) + (int64_t)up * N;
+            *reinterpret_cast<float4*>(Gs + ch) = make_float4(y[0], y[1], y[2], y[3]);
+          }
+        } else if (GATEUP) {
           // lanes with g < 2 hold gate channels 4g..4g+3, lane + 32 the same up channels
           float up[4];
 #pragma unroll
@@ -376,11 +388,52 @@ static hipError_t stream_dispatch(int max_rows, unsigned gy, hipStream_t st, con
                                                                   E, rows_cap, act, out);
 }
 
-hipError_t launch_stream_gateup(int w8, int max_rows, const bf16_bits* x, RouteView rv, const void* wg,
-                                const void* wu, const float* scales, int64_t T, int d, int f, int E, int act,
-                                bf16_bits* H, hipStream_t st) {
-  return w8 ? stream_dispatch<true, true>(max_rows, 1u, st, x, rv, wg, wu, scales, T, d, f, E, 0, act, H)
-            : stream_dispatch<true, false>(max_rows, 1u, st, x, rv, wg, wu, scales, T, d, f, E, 0, act, H);
+// H[r][c] = act(sum_s G[s][r][c]) * (sum_s G[s][r][f + c]) in fp32 (slices
+// added in ascending order), rounded to bf16, for the rows the permutation
+// filled (offsets[E]); four channels per thread.
+__global__ __launch_bounds__(256) void glu_splits_kernel(const float* __restrict__ G, int S, int64_t rows_cap,
+                                                         const int32_t* __restrict__ offsets, int E, int f, int act,
+                                                         bf16_bits* __restrict__ H) {
+  const int64_t rows = offsets[E];
+  const int64_t q = f / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * q; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / q;
+    const int c = (int)(i - r * q) * 4;
+    float gs[4] = {0.f, 0.f, 0.f, 0.f}, us[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s) {
+      const float* row = G + ((int64_t)s * rows_cap + r) * (2 * (int64_t)f);
+      const float4 a = *reinterpret_cast<const float4*>(row + c);
+      const float4 b = *reinterpret_cast<const float4*>(row + f + c);
+      gs[0] += a.x; gs[1] += a.y; gs[2] += a.z; gs[3] += a.w;
+      us[0] += b.x; us[1] += b.y; us[2] += b.z; us[3] += b.w;
+    }
+    float h[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) h[v] = glu_act(act, gs[v]) * us[v];
+    uint2 o;
+    o.x = pack_bf16x2(h[0], h[1]);
+    o.y = pack_bf16x2(h[2], h[3]);
+    *reinterpret_cast<uint2*>(H + r * f + c) = o;
+  }
+}
+
+hipError_t launch_stream_gateup(int w8, int max_rows, int splits, const bf16_bits* x, RouteView rv, const void* wg,
+                                const void* wu, const float* scales, int64_t T, int64_t rows_cap, int d, int f, int E,
+                                int act, bf16_bits* H, float* G, hipStream_t st) {
+  if (splits <= 1)
+    return w8 ? stream_dispatch<true, true>(max_rows, 1u, st, x, rv, wg, wu, scales, T, d, f, E, 0, act, H)
+              : stream_dispatch<true, false>(max_rows, 1u, st, x, rv, wg, wu, scales, T, d, f, E, 0, act, H);
+  const unsigned gy = (unsigned)splits;
+  const hipError_t err =
+      w8 ? stream_dispatch<true, true>(max_rows, gy, st, x, rv, wg, wu, scales, T, d, f, E, rows_cap, act, G)
+         : stream_dispatch<true, false>(max_rows, gy, st, x, rv, wg, wu, scales, T, d, f, E, rows_cap, act, G);
+  if (err != hipSuccess) return err;
+  int64_t blocks = (rows_cap * (f / 4) + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(glu_splits_kernel, dim3((unsigned)blocks), dim3(256), 0, st, G, splits, rows_cap, rv.offsets, E,
+                     f, act, H);
+  return hipGetLastError();
 }
 
 hipError_t launch_stream_down(int w8, int max_rows, int splits, const bf16_bits* H, RouteView rv, const void* wd,

@@ -66,6 +66,13 @@ def test_workspace_bytes():
     assert gm.grok_moe_workspace_bytes(8, 64, 64, 65, 2, gm.F32, gm.F32) == 0   # fp32 router: E <= 64
     # many experts: the router's split-K logits [S][T][E] fp64 are part of the workspace
     assert gm.grok_moe_workspace_bytes(8192, 7168, 2048, 256, 8) >= 8192 * 256 * 8
+    # fine-grained decode (256 experts of width 2048, top-8, 8 tokens: about 58 experts hit, 1,869
+    # gate/up workgroups): the gate/up reduction runs in two splits whose fp32 sums [2][64][4096]
+    # are part of the workspace, next to Y [64][7168] fp32
+    assert gm.grok_moe_workspace_bytes(8, 7168, 2048, 256, 8) >= 2 * 64 * 4096 * 4 + 64 * 7168 * 4
+    # 16 tokens (about 103 experts hit, 3,295 workgroups): one split, no such buffer (with it the
+    # workspace would hold at least G [2][128][4096] and Y [128][7168] fp32)
+    assert gm.grok_moe_workspace_bytes(16, 7168, 2048, 256, 8) < 2 * 128 * 4096 * 4 + 128 * 7168 * 4
     assert gm.grok_moe_workspace_bytes(8, 6144, 32768, 8, 2, gm.F32, gm.BF16) == 0   # dtype combo
 
 
