@@ -31,9 +31,11 @@
 // Gate/up pass: a wavefront owns 8 gate channels and the same 8 up channels
 // (16 weight rows, one 16x16x32 MFMA tile per 16 activation rows); lanes
 // holding gate results take the matching up results from lane + 32 and form
-// act(gate) * up (GELU, or SiLU for SwiGLU experts). Down pass: a wavefront owns 16 output channels, split over
-// the reduction into `gridDim.y` partial sums (fixed order, reduced by the
-// combine stage).
+// act(gate) * up (GELU, or SiLU for SwiGLU experts); with gridDim.y > 1
+// (fine-grained layers at small batches) each slice of the reduction writes
+// its fp32 gate and up sums instead, and glu_splits_kernel forms H. Down
+// pass: a wavefront owns 16 output channels, split over the reduction into
+// `gridDim.y` partial sums (fixed order, reduced by the combine stage).
 //
 // Fragment layout of v_mfma_f32_16x16x32_bf16: lane l supplies row (l mod 16)
 // and 8 reduction values of group l / 16; result register v of lane l is
