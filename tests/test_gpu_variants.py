@@ -224,6 +224,14 @@ def test_fine_grained_int8_and_capacity():
     assert (dbg["pos"][:, :8] == -1).any() and (dbg["pos"][:, 8] >= 0).all()   # shared expert never capped
 
 
+def test_fine_grained_split_gateup_with_capacity():
+    # 48 tokens over 256 experts with d = f = 256: the streaming gate/up runs in two reduction
+    # splits (fp32 sums + glu_splits_kernel), here with capped, skewed routing (drops) as well
+    w = synthetic.make("dsv3_decode", T=48, d=256, f=256, seed=9, capacity_factor=0.5, skew=True)
+    got, dbg, _ = _check(w, label="fine-grained split gate/up, capacity")
+    assert (dbg["pos"][:, :8] == -1).any() and (dbg["pos"][:, 8] >= 0).all()
+
+
 def test_fine_grained_routing_override():
     T, E = 50, 256
     # GELU experts: the oracle's forward_given_routing evaluates the GELU layer on a given routing
