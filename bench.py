@@ -11,6 +11,13 @@ Prints one JSON line with the whole-job throughput (tokens/s), the roofline of
 the dominant kernel measured live with HIP events on the launch stream, and
 the CPU oracle timed on the host as a reported baseline.
 
+The metric has two halves: HBM bandwidth at decode (T <= 64) and MFMA
+utilisation at one full 8192-token context. The default run measures both in
+one invocation: the decode step gives `value`, and the same resident weights
+(the prefill workload draws identical weights from the same seed) then run the
+8192-token prefill, reported under the "prefill" key with its own tokens/s,
+MFMA roofline and sampled CPU baseline. --no-prefill skips that half.
+
 Variants (not the headline): --workload mixtral_decode / mixtral_prefill (Mixtral
 8x22B expert shapes, SiLU experts, renormalised gates), dsv3_decode /
 dsv3_prefill (DeepSeek-V3-shape fine-grained layer: 256 routed experts of
@@ -68,6 +75,8 @@ def parse():
     ap.add_argument("--capacity", type=float, default=0.0,
                     help="capacity factor c > 0: each expert runs at most floor(c*k*T/E) assignments")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="default decode run only: skip the 8192-token prefill half of the metric")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens the oracle times (0 = default per workload)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="the oracle repeats its sample until this much wall time has passed")
@@ -183,6 +192,42 @@ def main():
                                         **variant)
         torch.cuda.synchronize()
         counts = dbg["counts"].cpu().numpy()
+    result = measure(torch, gm, HipEvents, w, (x, rw, wg, wu, wd, sc), variant, out, ws, stream, counts, workload,
+                     args)
+    result["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, name, args)
+    if name == "decode" and not (args.no_prefill or args.tokens or args.shard or args.sandwich or args.capacity):
+        # The MFMA half of the metric: one full 8192-token context through the same resident weights.
+        del ws, out, dbg
+        torch.cuda.empty_cache()
+        t0 = time.perf_counter()
+        wp = synthetic.make("prefill", with_weights=False)
+        assert wp.d == w.d and wp.f == w.f and wp.E == w.E and wp.k == w.k and np.array_equal(wp.router_w, w.router_w)
+        import dataclasses
+        wp = dataclasses.replace(wp, w_gate=w.w_gate, w_up=w.w_up, w_down=w.w_down, scales=w.scales)
+        xp = dev(wp.x)
+        outp = torch.empty_like(xp)
+        need = gm.grok_moe_workspace_bytes_ex(xp, rw, wg, wu, wd, k=wp.k, **variant)
+        wsp = torch.empty(need, dtype=torch.uint8, device="cuda")
+        _, dbgp = gm.grok_moe_forward_ex(xp, rw, wg, wu, wd, k=wp.k, scales=sc, out=outp, workspace=wsp, debug=True,
+                                         **variant)
+        torch.cuda.synchronize()
+        countsp = dbgp["counts"].cpu().numpy()
+        del dbgp
+        log(f"prefill: {wp.T} tokens resident in HBM ({time.perf_counter() - t0:.1f}s), rows per expert "
+            f"{countsp.tolist()}")
+        pre = measure(torch, gm, HipEvents, wp, (xp, rw, wg, wu, wd, sc), variant, outp, wsp, stream, countsp,
+                      WORKLOAD_NAMES["prefill"], args)
+        pre["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wp, "prefill", args)
+        for key in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data"):
+            pre.pop(key, None)
+        result["prefill"] = pre
+    print(json.dumps(result), flush=True)
+
+
+def measure(torch, gm, HipEvents, w, tensors, variant, out, ws, stream, counts, workload, args):
+    """Times exactly args.steps layer calls after args.warmup untimed ones; returns the bench record of one
+    workload (throughput, the dominant kernel's roofline from HIP events on the launch stream, stage times)."""
+    x, rw, wg, wu, wd, sc = tensors
     n_hit = int(np.sum(counts > 0))
     rows = int(counts.sum())
 
@@ -227,7 +272,8 @@ def main():
     # per-step device time (first stage event to last) over the breakdown pass
     q = np.percentile(np.array(step_ms), [10, 50, 90])
     step_dist = {"p10": round(float(q[0]), 5), "median": round(float(q[1]), 5), "p90": round(float(q[2]), 5)}
-    log("stage ms: " + ", ".join(f"{n}={v:.4f}" for n, v in stage_ms.items()))
+    log(f"{workload}: {ms_per_step:.4f} ms/step; stage ms: " +
+        ", ".join(f"{n}={v:.4f}" for n, v in stage_ms.items()))
 
     # algorithmic work of the dominant kernel (gate/up grouped GEMM + GELU*up):
     # per hit expert its two d x f weight matrices, plus the routed rows of x
@@ -255,12 +301,8 @@ def main():
     roof.update({"kernel": "gate_up grouped GEMM (+" + ("SiLU" if w.activation == "silu" else "GELU") + "*up)",
                  "algorithmic_per_launch": gu_bytes if hbm_bound else gu_flops,
                  "avg_launch_ms": round(gate_up_ms, 5), "traffic_source": traffic_note})
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, name, args)
-
-    result = {
+    layer_s = ms_per_step / 1e3
+    return {
         "metric": METRIC,
         "value": round(tokens_per_s, 2),
         "unit": "tokens/s",
@@ -275,49 +317,91 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k,
                    "weights": w.w_dtype, "experts_hit": n_hit, "activation": w.activation,
-                   "renormalize": w.renormalize, "capacity_factor": w.capacity_factor, "sandwich": args.sandwich,
+                   "renormalize": w.renormalize, "capacity_factor": w.capacity_factor,
+                   "sandwich": w.norm_pre is not None,
                    "n_shared": w.n_shared, "router_bias": w.router_bias is not None, "rows_run": rows,
                    "rows_per_expert": counts.tolist() if len(counts) <= 16 else None},
         "roofline": roof,
-        "cpu_baseline": cpu,
-        "layer": {"ms": round(ms_per_step, 5), "GBps": round(layer_bytes / (ms_per_step / 1e3) / 1e9, 1),
-                  "TFLOPs": round(layer_flops / (ms_per_step / 1e3) / 1e12, 2),
+        "layer": {"ms": round(ms_per_step, 5), "GBps": round(layer_bytes / layer_s / 1e9, 1),
+                  "TFLOPs": round(layer_flops / layer_s / 1e12, 2),
+                  "mfma_frac": round(layer_flops / layer_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                  "hbm_frac": round(layer_bytes / layer_s / 1e9 / HBM_PEAK_GBS, 4),
                   "stage_ms": {k2: round(v, 5) for k2, v in stage_ms.items()},
                   "device_step_ms": step_dist, "breakdown_steps": nb},
     }
-    print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(w, name, args):
-    """Times the CPU oracle on the host cores over a bounded sample of the same
-    batch: the first n tokens, whole layer, repeated until about
-    ``--cpu-seconds`` of wall time has passed."""
-    import oracle
-    n = args.cpu_sample or {"tiny_f32": 64}.get(name, 8)
-    n = min(n, w.T)
-    cores = oracle.threads()
-    log(f"timing the CPU oracle on {n} tokens with {cores} threads (about {args.cpu_seconds:.0f} s)")
-    passes, dt = 0, 0.0
-    t0 = time.perf_counter()
-    while passes == 0 or (dt < args.cpu_seconds and passes < 100000):
-        oracle.layer(w.x[:n], w.router_w, w.w_gate, w.w_up, w.w_down, w.k, scales=w.scales,
-                     activation=oracle.SILU if w.activation == "silu" else oracle.GELU, renormalize=w.renormalize,
-                     capacity_factor=w.capacity_factor, norm_pre=w.norm_pre, norm_post=w.norm_post,
-                     norm_eps=w.norm_eps, n_shared=w.n_shared, router_bias=w.router_bias, nthreads=cores)
-        passes += 1
-        dt = time.perf_counter() - t0
-    model = None
+def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
+                return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"value": round(n * passes / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "cpu_model": model, "host_cpus": os.cpu_count(),
-            "sample": f"first {n} of the {w.T} tokens as their own batch, {passes} pass(es), whole layer "
-                      f"(routing, {w.k} experts per token, combine) in fp64: {dt:.2f} s"}
+    return None
+
+
+def oracle_sample(perm, offsets, T, n=256, per_expert=8, seed=0):
+    """Seeded sample of n distinct tokens holding at least `per_expert` tokens of every expert that has
+    rows (fewer where an expert has fewer), the rest drawn uniformly from the remaining tokens."""
+    rng = np.random.default_rng(seed)
+    pick = set()
+    for e in range(len(offsets) - 1):
+        toks = np.unique(perm[offsets[e]:offsets[e + 1]])
+        if len(toks):
+            pick.update(int(t) for t in rng.choice(toks, size=min(per_expert, len(toks)), replace=False))
+    rest = np.setdiff1d(np.arange(T), np.fromiter(pick, dtype=np.int64, count=len(pick)))
+    extra = max(0, min(n, T) - len(pick))
+    pick.update(int(t) for t in rng.choice(rest, size=min(extra, len(rest)), replace=False))
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def cpu_baseline(w, name, args):
+    """Times the CPU oracle on the host cores over a bounded sample of the same batch.
+
+    Up to 256 tokens: the whole batch, whole layer, repeated until about ``--cpu-seconds`` of wall time
+    has passed. Larger batches: routing and permutation of every token, then the expert outputs of a
+    seeded sample of 256 tokens with at least 8 per expert that has rows; the rate is T over (routing and
+    permutation time + sample time x T / 256)."""
+    import oracle
+    cores = oracle.threads()
+    act = oracle.SILU if w.activation == "silu" else oracle.GELU
+    sampled = w.T > 256 and not (w.n_shared or w.norm_pre is not None or w.capacity_factor or w.renormalize
+                                 or w.router_bias is not None)
+    if not sampled:
+        n = min(args.cpu_sample or {"tiny_f32": 64}.get(name, w.T if w.T <= 256 else 8), w.T)
+        log(f"timing the CPU oracle on {n} tokens with {cores} threads (at least {args.cpu_seconds:.0f} s)")
+        passes, dt = 0, 0.0
+        t0 = time.perf_counter()
+        while passes == 0 or (dt < args.cpu_seconds and passes < 100000):
+            oracle.layer(w.x[:n], w.router_w, w.w_gate, w.w_up, w.w_down, w.k, scales=w.scales, activation=act,
+                         renormalize=w.renormalize, capacity_factor=w.capacity_factor, norm_pre=w.norm_pre,
+                         norm_post=w.norm_post, norm_eps=w.norm_eps, n_shared=w.n_shared,
+                         router_bias=w.router_bias, nthreads=cores)
+            passes += 1
+            dt = time.perf_counter() - t0
+        return {"value": round(n * passes / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
+                "sample": f"{'all' if n == w.T else f'first {n} of the'} {w.T} tokens as one batch, {passes} "
+                          f"pass(es), whole layer (routing, {w.k} experts per token, combine) in fp64: {dt:.2f} s"}
+    n = args.cpu_sample or 256
+    log(f"timing the CPU oracle: routing + permutation of {w.T} tokens, expert outputs of a {n}-token sample, "
+        f"{cores} threads")
+    t0 = time.perf_counter()
+    _, idx, gate = oracle.route(w.x, w.router_w, w.k, nthreads=cores)
+    _, offsets, perm, _ = oracle.permute(idx, w.E)
+    t_route = time.perf_counter() - t0
+    tokens = oracle_sample(perm, offsets, w.T, n=n)
+    t0 = time.perf_counter()
+    oracle.forward_given_routing(w.x, w.w_gate, w.w_up, w.w_down, idx, gate, scales=w.scales, tokens=tokens,
+                                 nthreads=cores)
+    t_exp = time.perf_counter() - t0
+    projected = t_route + t_exp * w.T / len(tokens)
+    return {"value": round(w.T / projected, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"routing + permutation of all {w.T} tokens in fp64 ({t_route:.2f} s), then the {w.k} expert "
+                      f"outputs and combine of a seeded {len(tokens)}-token sample with >= 8 tokens per expert "
+                      f"({t_exp:.2f} s); value = {w.T} / (routing time + sample time x {w.T}/{len(tokens)})"}
 
 
 def _source_digest(files):

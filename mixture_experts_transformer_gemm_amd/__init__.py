@@ -94,8 +94,9 @@ def grok_moe_workspace_bytes(T: int, d: int, f: int, E: int, k: int, act_dtype: 
 
 
 def grok_moe_workspace_bytes_ex(x, router_w, w_gate, w_up, w_down, k: int = 2, **variant) -> int:
-    """Workspace bytes of one grok_moe_forward_ex call with these tensors and variant knobs."""
-    a = make_args(x, router_w, w_gate, w_up, w_down, x, k, **variant)   # out: only its shape is read here
+    """Workspace bytes of one grok_moe_forward_ex call with these tensors and variant knobs (sizing only:
+    the 8-bit scales may be left out, and x stands in for out)."""
+    a = make_args(x, router_w, w_gate, w_up, w_down, x, k, sizing=True, **variant)
     return int(lib().grok_moe_workspace_bytes_ex(ctypes.byref(a)))
 
 
@@ -128,6 +129,7 @@ def _dtype_code(t) -> int:
 
 
 def _check_tensors(named: Dict[str, object]):
+    dev = None
     for name, t in named.items():
         if t is None:
             continue
@@ -135,38 +137,91 @@ def _check_tensors(named: Dict[str, object]):
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
 
 
 def _shape(x, w_gate, router_w, n_shared: int = 0):
     """(T, d, f, E routed); the weights hold E + n_shared experts."""
+    if x.dim() != 2 or w_gate.dim() != 3:
+        raise ValueError("x must be [T, d] and w_gate [E, f, d]")
     T, d = x.shape
     Et, f, d2 = w_gate.shape
     E = Et - n_shared
     if d2 != d:
         raise ValueError(f"w_gate is [E, f, d] with d={d2}, x has d={d}")
+    if E < 1:
+        raise ValueError(f"w_gate holds {Et} experts, fewer than n_shared + 1 = {n_shared + 1}")
     if router_w is not None and tuple(router_w.shape) != (E, d):
         raise ValueError(f"router_w must be [E, d] = [{E}, {d}], got {tuple(router_w.shape)}")
     return T, d, f, E
 
 
-def make_args(x, router_w, w_gate, w_up, w_down, out, k: int, scales=None, route_idx=None,
-              route_gate=None, activation: int = ACT_GELU, renormalize: bool = False,
-              capacity_factor: float = 0.0, norm_pre=None, norm_post=None, norm_eps: float = 1e-5,
-              n_shared: int = 0, router_bias=None) -> Args:
+def _validate(x, router_w, w_gate, w_up, w_down, out, k: int, scales=None, route_idx=None, route_gate=None,
+              norm_pre=None, norm_post=None, n_shared: int = 0, router_bias=None, want_w=None,
+              sizing: bool = False):
+    """Checks every tensor's device, contiguity, shape and dtype against the layout of include/grok_moe.h
+    before anything reaches the library (which sees only pointers and sizes). want_w: the weight dtype a
+    plain entry point requires (None: any supported combination). sizing: the call only sizes a workspace
+    (8-bit scales may be absent). Returns (T, d, f, E routed)."""
+    torch = _torch()
     T, d, f, E = _shape(x, w_gate, router_w, n_shared)
     Et = E + n_shared
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
+    wdt = w_gate.dtype
+    if want_w is not None and wdt != want_w:
+        raise TypeError(f"this entry point takes {want_w} expert weights, got {wdt}")
+    ok = {torch.bfloat16: (torch.bfloat16, torch.int8), torch.float32: (torch.float32,)}[x.dtype]
+    if wdt not in ok:
+        raise TypeError(f"{x.dtype} activations take expert weights of {ok}, got {wdt}")
     if tuple(w_up.shape) != (Et, f, d) or tuple(w_down.shape) != (Et, d, f):
-        raise ValueError("w_up must be [E + n_shared, f, d] and w_down [E + n_shared, d, f]")
-    if router_bias is not None and (tuple(router_bias.shape) != (E,) or router_bias.dtype != _torch().float32):
+        raise ValueError(f"w_up must be [E + n_shared, f, d] = [{Et}, {f}, {d}] and w_down [{Et}, {d}, {f}], got "
+                         f"{tuple(w_up.shape)} and {tuple(w_down.shape)}")
+    if w_up.dtype != wdt or w_down.dtype != wdt:
+        raise TypeError(f"w_gate, w_up and w_down must share one dtype ({wdt}, {w_up.dtype}, {w_down.dtype})")
+    if router_w is not None and router_w.dtype != x.dtype:
+        raise TypeError(f"router_w must have the activation dtype {x.dtype}, got {router_w.dtype}")
+    if tuple(out.shape) != (T, d) or out.dtype != x.dtype:
+        raise ValueError(f"out must be [T, d] = [{T}, {d}] of dtype {x.dtype}, got {tuple(out.shape)} {out.dtype}")
+    if wdt == torch.int8:
+        n = 2 * Et * f + Et * d
+        if scales is None and sizing:
+            pass
+        elif scales is None or scales.dtype != torch.float32 or scales.numel() != n:
+            raise ValueError(f"int8 weights need float32 scales of 2*E*f + E*d = {n} values (gate | up | down)")
+    elif scales is not None:
+        raise ValueError("scales are only taken with int8 weights")
+    if (route_idx is None) != (route_gate is None):
+        raise ValueError("route_idx and route_gate go together")
+    if route_idx is not None:
+        if tuple(route_idx.shape) != (T, k) or route_idx.dtype != torch.int32:
+            raise ValueError(f"route_idx must be [T, k] = [{T}, {k}] int32")
+        if tuple(route_gate.shape) != (T, k) or route_gate.dtype != torch.float32:
+            raise ValueError(f"route_gate must be [T, k] = [{T}, {k}] float32")
+    elif router_w is None:
+        raise ValueError("router_w is needed unless a routing (route_idx, route_gate) is given")
+    if router_bias is not None and (tuple(router_bias.shape) != (E,) or router_bias.dtype != torch.float32):
         raise ValueError(f"router_bias must be [E] = [{E}] float32")
-    if tuple(out.shape) != (T, d):
-        raise ValueError("out must be [T, d]")
+    if (norm_pre is None) != (norm_post is None):
+        raise ValueError("norm_pre and norm_post go together")
     for name, g in (("norm_pre", norm_pre), ("norm_post", norm_post)):
         if g is not None and (tuple(g.shape) != (d,) or g.dtype != x.dtype):
             raise ValueError(f"{name} must be [d] = [{d}] of the activation dtype")
     _check_tensors(dict(x=x, router_w=router_w, w_gate=w_gate, w_up=w_up, w_down=w_down, out=out, scales=scales,
                         route_idx=route_idx, route_gate=route_gate, norm_pre=norm_pre, norm_post=norm_post,
                         router_bias=router_bias))
+    return T, d, f, E
+
+
+def make_args(x, router_w, w_gate, w_up, w_down, out, k: int, scales=None, route_idx=None,
+              route_gate=None, activation: int = ACT_GELU, renormalize: bool = False,
+              capacity_factor: float = 0.0, norm_pre=None, norm_post=None, norm_eps: float = 1e-5,
+              n_shared: int = 0, router_bias=None, sizing: bool = False) -> Args:
+    T, d, f, E = _validate(x, router_w, w_gate, w_up, w_down, out, k, scales, route_idx, route_gate, norm_pre,
+                           norm_post, n_shared, router_bias, sizing=sizing)
     a = Args()
     a.x, a.router_w, a.w_gate, a.w_up, a.w_down = _ptr(x), _ptr(router_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down)
     a.scales, a.out = _ptr(scales), _ptr(out)
@@ -190,8 +245,9 @@ def grok_moe_forward(x, router_w, w_gate, w_up, w_down, out=None, k: int = 2, st
     torch = _torch()
     if out is None:
         out = torch.empty_like(x)
-    T, d, f, E = _shape(x, w_gate, router_w)
-    _check_tensors(dict(x=x, router_w=router_w, w_gate=w_gate, w_up=w_up, w_down=w_down, out=out))
+    T, d, f, E = _validate(x, router_w, w_gate, w_up, w_down, out, k, want_w=torch.bfloat16)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("grok_moe_forward takes bfloat16 activations")
     rc = lib().grok_moe_forward(_ptr(x), _ptr(router_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out), T, d,
                                 f, E, k, _stream(stream))
     _raise(rc, "grok_moe_forward")
@@ -203,8 +259,7 @@ def grok_moe_forward_w8(x, router_w, w_gate, w_up, w_down, scales, out=None, k: 
     torch = _torch()
     if out is None:
         out = torch.empty_like(x)
-    T, d, f, E = _shape(x, w_gate, router_w)
-    _check_tensors(dict(x=x, router_w=router_w, w_gate=w_gate, w_up=w_up, w_down=w_down, out=out, scales=scales))
+    T, d, f, E = _validate(x, router_w, w_gate, w_up, w_down, out, k, scales=scales, want_w=torch.int8)
     rc = lib().grok_moe_forward_w8(_ptr(x), _ptr(router_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(scales),
                                    _ptr(out), T, d, f, E, k, _stream(stream))
     _raise(rc, "grok_moe_forward_w8")
@@ -216,8 +271,7 @@ def grok_moe_forward_f32(x, router_w, w_gate, w_up, w_down, out=None, k: int = 2
     torch = _torch()
     if out is None:
         out = torch.empty_like(x)
-    T, d, f, E = _shape(x, w_gate, router_w)
-    _check_tensors(dict(x=x, router_w=router_w, w_gate=w_gate, w_up=w_up, w_down=w_down, out=out))
+    T, d, f, E = _validate(x, router_w, w_gate, w_up, w_down, out, k, want_w=torch.float32)
     rc = lib().grok_moe_forward_f32(_ptr(x), _ptr(router_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out), T,
                                     d, f, E, k, _stream(stream))
     _raise(rc, "grok_moe_forward_f32")
@@ -245,31 +299,38 @@ def grok_moe_forward_ex(x, router_w, w_gate, w_up, w_down, k: int = 2, scales=No
     need = int(lib().grok_moe_workspace_bytes_ex(ctypes.byref(a)))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    dbg = {}
-    dptr = None
-    if debug or events:
-        d = Debug()
-        if debug:
-            T, E, K = a.T, a.E + n_shared, k + n_shared
-            dbg = dict(idx=torch.full((T, K), -7, dtype=torch.int32, device=dev),
-                       gate=torch.full((T, K), -7.0, dtype=torch.float32, device=dev),
-                       counts=torch.full((E,), -7, dtype=torch.int32, device=dev),
-                       offsets=torch.full((E + 1,), -7, dtype=torch.int32, device=dev),
-                       perm=torch.full((T * K,), -7, dtype=torch.int32, device=dev),
-                       pos=torch.full((T, K), -7, dtype=torch.int32, device=dev))
-            if norm_pre is not None:
-                dbg["u"] = torch.empty_like(x)
-            for name, t in dbg.items():
-                setattr(d, name, t.data_ptr())
-        if events:
-            for i, ev in enumerate(events[:6]):
-                if ev:
-                    d.events[i] = ctypes.c_void_p(int(ev))
-        dptr = ctypes.byref(d)
+    dbg, dptr = _debug(a, k, n_shared, norm_pre is not None, dev, debug, events)
     rc = lib().grok_moe_forward_ex(ctypes.byref(a), workspace.data_ptr(), workspace.numel(), dptr,
                                    _stream(stream))
     _raise(rc, "grok_moe_forward_ex")
     return out, dbg
+
+
+def _debug(a, k, n_shared, sandwich, dev, debug, events):
+    """Debug struct (device arrays for the routing intermediates, event handles) or (dict(), None)."""
+    torch = _torch()
+    dbg = {}
+    if not (debug or events):
+        return dbg, None
+    d = Debug()
+    if debug:
+        T, E, K = a.T, a.E + n_shared, k + n_shared
+        dbg = dict(idx=torch.full((T, K), -7, dtype=torch.int32, device=dev),
+                   gate=torch.full((T, K), -7.0, dtype=torch.float32, device=dev),
+                   counts=torch.full((E,), -7, dtype=torch.int32, device=dev),
+                   offsets=torch.full((E + 1,), -7, dtype=torch.int32, device=dev),
+                   perm=torch.full((T * K,), -7, dtype=torch.int32, device=dev),
+                   pos=torch.full((T, K), -7, dtype=torch.int32, device=dev))
+        if sandwich:
+            dbg["u"] = torch.empty((a.T, a.d), dtype=torch.bfloat16 if a.act_dtype == BF16 else torch.float32,
+                                   device=dev)
+        for name, t in dbg.items():
+            setattr(d, name, t.data_ptr())
+    if events:
+        for i, ev in enumerate(events[:6]):
+            if ev:
+                d.events[i] = ctypes.c_void_p(int(ev))
+    return dbg, ctypes.byref(d)
 
 
 # ---------------------------------------------------------------- HIP events (timing plumbing)

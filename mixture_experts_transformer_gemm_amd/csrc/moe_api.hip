@@ -8,6 +8,7 @@
 
 using namespace gmoe;
 
+
 namespace {
 
 enum Path { PATH_F32 = 0, PATH_TILED = 2, PATH_STREAM = 3 };

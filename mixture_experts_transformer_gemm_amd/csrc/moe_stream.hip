@@ -52,7 +52,6 @@ namespace gmoe {
 
 namespace {
 
-constexpr int kSB = 64;      // reduction values per stage
 constexpr int kRowB = 128;   // LDS bytes per row and stage
 
 // 16 bytes per lane straight into LDS with the nontemporal cache policy:

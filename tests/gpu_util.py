@@ -54,6 +54,17 @@ def normwise_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(got - ref).max(1) / den))
 
 
+def elementwise_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max over elements of |got - ref| / max(|ref|, 1e-3 * ||ref_t||_inf): the elementwise relative error,
+    with entries near zero measured against a thousandth of their token's largest value."""
+    if got.size == 0:
+        return 0.0
+    floor = 1e-3 * np.abs(ref).max(1, keepdims=True)
+    den = np.maximum(np.abs(ref), floor)
+    den = np.where(den > 0, den, 1.0)
+    return float(np.max(np.abs(got - ref) / den))
+
+
 def check_routing(gidx: np.ndarray, ggate: np.ndarray, probs: np.ndarray):
     """GPU routing vs oracle probabilities: at each rank the chosen expert's oracle probability is
     within TIE_WINDOW of the oracle's rank-j probability, indices are distinct, and the GPU gate

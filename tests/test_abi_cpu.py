@@ -225,3 +225,76 @@ def test_build_rejects_scratch_kernels():
         "x.hip:2:1: remark:     ScratchSize [bytes/lane]: 336 [-Rpass-analysis=kernel-resource-usage]",
     ])
     assert scratch_kernels(remarks) == [("_Z1bv", 336)]
+
+
+def _cpu_layer(T=4, d=64, f=128, E=4, wdt="bf16"):
+    torch = pytest.importorskip("torch")
+    adt = torch.float32 if wdt == "f32" else torch.bfloat16
+    w = {"bf16": torch.bfloat16, "f32": torch.float32, "i8": torch.int8}[wdt]
+    t = dict(x=torch.zeros(T, d, dtype=adt), router_w=torch.zeros(E, d, dtype=adt),
+             w_gate=torch.zeros(E, f, d, dtype=w), w_up=torch.zeros(E, f, d, dtype=w),
+             w_down=torch.zeros(E, d, f, dtype=w), out=torch.zeros(T, d, dtype=adt))
+    return torch, t
+
+
+@pytest.mark.parametrize("case", ["out_shape", "out_dtype", "up_shape", "down_shape", "down_dtype", "router_dtype",
+                                  "scales_len", "scales_dtype", "scales_missing", "scales_bf16", "route_idx_dtype",
+                                  "route_gate_shape", "route_alone", "norm_alone", "act_dtype"])
+def test_binding_rejects_bad_tensors_before_the_library(case):
+    # every tensor's shape and dtype is checked before a pointer reaches the library, which cannot check
+    # sizes; these raise on host tensors, before the device check, so no GPU is needed
+    wdt = "i8" if case.startswith("scales") and case != "scales_bf16" else "bf16"
+    torch, t = _cpu_layer(wdt=wdt)
+    T, d, f, E = 4, 64, 128, 4
+    kw = {}
+    if wdt == "i8":
+        kw["scales"] = torch.zeros(2 * E * f + E * d, dtype=torch.float32)
+    if case == "out_shape":
+        t["out"] = torch.zeros(T, d + 1, dtype=torch.bfloat16)
+    elif case == "out_dtype":
+        t["out"] = torch.zeros(T, d, dtype=torch.float32)
+    elif case == "up_shape":
+        t["w_up"] = torch.zeros(E, f, d + 8, dtype=torch.bfloat16)
+    elif case == "down_shape":
+        t["w_down"] = torch.zeros(E, f, d, dtype=torch.bfloat16)
+    elif case == "down_dtype":
+        t["w_down"] = torch.zeros(E, d, f, dtype=torch.float32)
+    elif case == "router_dtype":
+        t["router_w"] = torch.zeros(E, d, dtype=torch.float32)
+    elif case == "scales_len":
+        kw["scales"] = torch.zeros(2 * E * f + E * d - 1, dtype=torch.float32)
+    elif case == "scales_dtype":
+        kw["scales"] = torch.zeros(2 * E * f + E * d, dtype=torch.bfloat16)
+    elif case == "scales_missing":
+        kw.pop("scales")
+    elif case == "scales_bf16":
+        kw["scales"] = torch.zeros(2 * E * f + E * d, dtype=torch.float32)
+    elif case == "route_idx_dtype":
+        kw["route_idx"] = torch.zeros(T, 2, dtype=torch.int64)
+        kw["route_gate"] = torch.zeros(T, 2, dtype=torch.float32)
+    elif case == "route_gate_shape":
+        kw["route_idx"] = torch.zeros(T, 2, dtype=torch.int32)
+        kw["route_gate"] = torch.zeros(T, 3, dtype=torch.float32)
+    elif case == "route_alone":
+        kw["route_idx"] = torch.zeros(T, 2, dtype=torch.int32)
+    elif case == "norm_alone":
+        kw["norm_pre"] = torch.zeros(d, dtype=torch.bfloat16)
+    elif case == "act_dtype":
+        t["x"] = torch.zeros(T, d, dtype=torch.float16)
+    with pytest.raises((ValueError, TypeError)) as ei:
+        gm.make_args(t["x"], t["router_w"], t["w_gate"], t["w_up"], t["w_down"], t["out"], 2, **kw)
+    assert "device" not in str(ei.value)
+
+
+def test_plain_wrappers_check_the_weight_dtype():
+    torch, t = _cpu_layer(wdt="f32")
+    with pytest.raises(TypeError):
+        gm.grok_moe_forward(t["x"], t["router_w"], t["w_gate"], t["w_up"], t["w_down"], out=t["out"])
+    with pytest.raises(TypeError):
+        gm.grok_moe_forward_w8(t["x"], t["router_w"], t["w_gate"], t["w_up"], t["w_down"], None, out=t["out"])
+    torch, t = _cpu_layer(wdt="bf16")
+    with pytest.raises(TypeError):
+        gm.grok_moe_forward_f32(t["x"], t["router_w"], t["w_gate"], t["w_up"], t["w_down"], out=t["out"])
+    t["out"] = torch.zeros(3, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        gm.grok_moe_forward(t["x"], t["router_w"], t["w_gate"], t["w_up"], t["w_down"], out=t["out"])

@@ -45,3 +45,23 @@ def test_traffic_lookup_checks_the_kernel_sources(tmp_path, monkeypatch):
 def test_every_bench_workload_has_a_generator_entry(wl):
     import synthetic
     assert wl in synthetic.WORKLOADS
+
+
+def test_oracle_sample_covers_every_expert():
+    # the CPU baseline's sample for large batches: n distinct tokens, at least 8 of every expert with rows
+    import numpy as np
+    rng = np.random.default_rng(5)
+    T, E, k = 3000, 8, 2
+    keys = rng.random((T, E)) * (1.0 + 5.0 * (np.arange(E) < 2))     # skewed toward experts 0 and 1
+    idx = np.argsort(-keys, axis=1)[:, :k]
+    idx[:3] = [[6, 7], [7, 5], [5, 6]]                                 # experts 5..7 get few tokens
+    order = np.lexsort((np.repeat(np.arange(T), k), idx.ravel()))
+    perm = np.repeat(np.arange(T), k)[order]
+    counts = np.bincount(idx.ravel(), minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    s = bench.oracle_sample(perm, offsets, T, n=256, per_expert=8, seed=0)
+    assert len(s) == 256 and len(np.unique(s)) == 256 and s.min() >= 0 and s.max() < T
+    for e in range(E):
+        have = np.isin(s, perm[offsets[e]:offsets[e + 1]]).sum()
+        assert have >= min(8, counts[e]), (e, have)
+    assert np.array_equal(s, bench.oracle_sample(perm, offsets, T, n=256, per_expert=8, seed=0))

@@ -2,9 +2,12 @@
 launch configuration the bench times (grok_moe_forward_ex with a caller workspace).
 
 All tokens are checked for routing and permutation; outputs are compared with
-the oracle on every token for the decode workload and on a seeded sample that
-covers every expert (first and last row of each segment plus random tokens) for
-the larger ones.
+the oracle on every token for the decode workloads and, for the larger ones, on
+a seeded sample: the first and last row of every row tile the tiled kernels run
+(every expert segment cut into tiles of the tile height the library picks for
+that workload) and random tokens. Both the
+per-token normwise error (the tolerance) and the elementwise error with a floor
+of a thousandth of the token's largest value are computed and printed.
 """
 import gc
 
@@ -13,25 +16,50 @@ import pytest
 
 import oracle
 import synthetic
-from gpu_util import TOL, check_permutation, check_routing, normwise_err, run_layer
+from gpu_util import TOL, check_permutation, check_routing, elementwise_err, normwise_err, run_layer
 
 torch = pytest.importorskip("torch")
 
 pytestmark = pytest.mark.gpu
 
 
-def _sample_tokens(dbg, E, n_random, seed):
+def _tile_rows(count, bm):
+    """Rows (within a segment of `count` rows) at the edges of each bm-row tile."""
+    rows = set()
+    for m0 in range(0, count, bm):
+        rows.update((m0, min(count, m0 + bm) - 1))
+    return rows
+
+
+def _sample_tokens(dbg, E, n_random, seed, bm=None):
+    """Tokens whose rows sit at the first and last row of every bm-row tile of every expert segment (bm None:
+    the segment edges only), plus n_random seeded tokens."""
     offs, perm = dbg["offsets"], dbg["perm"]
     pick = []
     for e in range(E):
-        if offs[e + 1] > offs[e]:
-            pick += [int(perm[offs[e]]), int(perm[offs[e + 1] - 1])]
+        n = int(offs[e + 1] - offs[e])
+        if n == 0:
+            continue
+        rows = {0, n - 1} if bm is None else _tile_rows(n, bm)
+        pick += [int(perm[offs[e] + r]) for r in sorted(rows)]
     T = dbg["idx"].shape[0]
     pick += list(np.random.default_rng(seed).choice(T, size=min(n_random, T), replace=False))
     return sorted(set(pick))
 
 
-def _run_and_check(name, n_random=8, T=None):
+def _tile_height(w):
+    """Row-tile height the library's plan picks for this shape (average rows per expert r): 64 up to 32
+    rows, 128 up to 96, 256 beyond, 320 past 256 rows with bf16 weights; 8-bit weights use 128 up to 384."""
+    r = w.T * w.k // w.E
+    bm = 64 if r <= 32 else (128 if r <= 96 else 256)
+    if w.w_dtype == "bf16" and r > 256:
+        bm = 320
+    if w.w_dtype == "i8" and r <= 384:
+        bm = 128
+    return bm
+
+
+def _run_and_check(name, n_random=8, T=None, tiles=True):
     print(f"[fullsize] generating workload {name} (T={T or 'default'})", flush=True)
     w = synthetic.make(name, T=T)
     print(f"[fullsize] {name}: T={w.T} d={w.d} f={w.f} E={w.E} k={w.k} weights={w.w_dtype}", flush=True)
@@ -43,13 +71,15 @@ def _run_and_check(name, n_random=8, T=None):
     check_permutation(dbg["idx"], dbg, w.E)
     assert np.all(np.isfinite(got))
     gates = np.take_along_axis(probs, dbg["idx"].astype(np.int64), 1)
-    tokens = None if w.T <= 8 else _sample_tokens(dbg, w.E, n_random, seed=w.T)
+    tokens = None if w.T <= 8 else _sample_tokens(dbg, w.E, n_random, seed=w.T, bm=_tile_height(w) if tiles else None)
     ref = oracle.forward_given_routing(w.x, w.w_gate, w.w_up, w.w_down, dbg["idx"], gates, scales=w.scales,
                                        tokens=tokens)
     sub = got if tokens is None else got[tokens]
     err = normwise_err(sub, ref)
+    ew = elementwise_err(sub, ref)
     tol = TOL["i8" if w.w_dtype == "i8" else "bf16"]
-    print(f"[fullsize] {name}: {len(sub)} tokens checked, normwise error {err:.3e} (tol {tol})", flush=True)
+    print(f"[fullsize] {name}: {len(sub)} tokens checked, normwise error {err:.3e} (tol {tol}), elementwise "
+          f"error {ew:.3e}", flush=True)
     assert err <= tol
     counts = dbg["counts"].copy()
     del w, got
@@ -95,5 +125,5 @@ def test_prefill_T32768_full():
     # four times the prefill batch: 65,536 rows, 26 row tiles of 320 per expert (53,248 gate/up
     # workgroups), and 4,992 down tiles (19.5 rounds of 256 CUs), so the down reduction runs in two
     # splits; every token's routing and the permutation are checked, outputs on a sample
-    dbg, counts = _run_and_check("prefill", n_random=4, T=32768)
+    dbg, counts = _run_and_check("prefill", n_random=4, T=32768, tiles=False)
     assert counts.sum() == 2 * 32768

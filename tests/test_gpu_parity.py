@@ -174,6 +174,22 @@ def test_binding_errors_raise():
     with pytest.raises(gm.GrokMoeError) as ei:
         gm.grok_moe_forward_ex(dev["x"], dev["router_w"], dev["w_gate"], dev["w_up"], dev["w_down"], workspace=ws)
     assert ei.value.code == gm.EWORKSPACE
+    # sizes the library cannot check are checked by the binding before any launch: a wrong-shape out
+    # and wrong-length 8-bit scales raise, and the out buffer is left untouched
+    out = torch.full((w.T, w.d + 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        gm.grok_moe_forward(dev["x"], dev["router_w"], dev["w_gate"], dev["w_up"], dev["w_down"], out=out)
+    with pytest.raises(ValueError):
+        gm.grok_moe_forward_ex(dev["x"], dev["router_w"], dev["w_gate"], dev["w_up"], dev["w_down"], out=out)
+    w8 = synthetic.make("int8", T=4, d=256, f=256)
+    d8 = dev_workload(w8, torch)
+    short = d8["scales"][:-1].contiguous()
+    with pytest.raises(ValueError):
+        gm.grok_moe_forward_w8(d8["x"], d8["router_w"], d8["w_gate"], d8["w_up"], d8["w_down"], short)
+    with pytest.raises(ValueError):
+        gm.grok_moe_forward_ex(d8["x"], d8["router_w"], d8["w_gate"], d8["w_up"], d8["w_down"], scales=short)
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all())
 
 
 @pytest.mark.parametrize("T", [40, 2049])
