@@ -196,6 +196,22 @@ int grok_moe_forward_f32(const float* x, const float* router_w, const float* w_g
                          const float* w_down, float* out, int64_t T, int64_t d, int64_t f, int32_t E, int32_t k,
                          void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the layer of
+ * grok_moe_forward_ex with the same kernels, its workspace taken from a
+ * static device array of GROK_MOE_STATIC_WORKSPACE_BYTES bytes that the
+ * library holds on each device it runs on until the process ends. Calls no
+ * allocating routine. Returns GROK_MOE_EWORKSPACE (enqueuing nothing) when
+ * this shape needs more workspace than that (grok_moe_workspace_bytes_ex());
+ * 64 MiB holds, for example, the Grok-1 layer (d = 6144, f = 32768, E = 8,
+ * k = 2, bf16 or 8-bit weights) up to T = 128 tokens. The array belongs to the current
+ * device, which must be the stream's. Every call on a device shares that
+ * device's array: calls that overlap in time on one device (on different
+ * streams, or from different host threads without ordering) race and give
+ * wrong results; calls ordered on one stream are safe. dbg may be NULL. */
+#define GROK_MOE_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+int grok_moe_forward_static(const grok_moe_args* a, const grok_moe_debug* dbg, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* grok_moe_status_string(int status);
 

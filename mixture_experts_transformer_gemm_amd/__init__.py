@@ -10,6 +10,8 @@ shapes:
 * ``grok_moe_forward_f32`` fp32 everything
 * ``grok_moe_forward_ex``  any of the above with caller workspace, optional
   routing override and debug outputs
+* ``grok_moe_forward_static`` the ``_ex`` layer with the library's static
+  per-device workspace (no allocation; shapes up to STATIC_WORKSPACE_BYTES)
 * ``grok_moe_workspace_bytes``, ``grok_moe_status_string``
 
 Layouts: x, out [T, d]; router_w [E, d]; w_gate, w_up [E, f, d]; w_down [E, d, f].
@@ -30,7 +32,8 @@ OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
 STAGES = ("router", "permute", "gate_up", "down", "combine")
 
 EXPORTED = ("grok_moe_workspace_bytes", "grok_moe_workspace_bytes_ex", "grok_moe_forward_ex", "grok_moe_forward",
-            "grok_moe_forward_w8", "grok_moe_forward_f32", "grok_moe_status_string")
+            "grok_moe_forward_w8", "grok_moe_forward_f32", "grok_moe_forward_static", "grok_moe_status_string")
+STATIC_WORKSPACE_BYTES = 64 << 20   # GROK_MOE_STATIC_WORKSPACE_BYTES
 
 
 class GrokMoeError(RuntimeError):
@@ -76,7 +79,9 @@ def lib():
         h.grok_moe_forward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
         h.grok_moe_forward_w8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
         h.grok_moe_forward_f32.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
-        for n in ("grok_moe_forward_ex", "grok_moe_forward", "grok_moe_forward_w8", "grok_moe_forward_f32"):
+        h.grok_moe_forward_static.argtypes = [ctypes.POINTER(Args), ctypes.POINTER(Debug), vp]
+        for n in ("grok_moe_forward_ex", "grok_moe_forward", "grok_moe_forward_w8", "grok_moe_forward_f32",
+                  "grok_moe_forward_static"):
             getattr(h, n).restype = ctypes.c_int
         h.grok_moe_status_string.argtypes = [ctypes.c_int]
         h.grok_moe_status_string.restype = ctypes.c_char_p
@@ -303,6 +308,27 @@ def grok_moe_forward_ex(x, router_w, w_gate, w_up, w_down, k: int = 2, scales=No
     rc = lib().grok_moe_forward_ex(ctypes.byref(a), workspace.data_ptr(), workspace.numel(), dptr,
                                    _stream(stream))
     _raise(rc, "grok_moe_forward_ex")
+    return out, dbg
+
+
+def grok_moe_forward_static(x, router_w, w_gate, w_up, w_down, k: int = 2, scales=None, out=None,
+                            route_idx=None, route_gate=None, debug: bool = False,
+                            events: Optional[Sequence[object]] = None, stream=None, activation: int = ACT_GELU,
+                            renormalize: bool = False, capacity_factor: float = 0.0, norm_pre=None,
+                            norm_post=None, norm_eps: float = 1e-5, n_shared: int = 0, router_bias=None):
+    """grok_moe_forward_ex without a workspace argument: the library uses its static per-device workspace
+    (STATIC_WORKSPACE_BYTES; larger shapes raise GrokMoeError with EWORKSPACE). Calls that overlap in time on
+    one device race on that workspace. Returns (out, dbg) like grok_moe_forward_ex (`out` must be given
+    when the caller cannot allocate)."""
+    torch = _torch()
+    dev = x.device
+    if out is None:
+        out = torch.empty_like(x)
+    a = make_args(x, router_w, w_gate, w_up, w_down, out, k, scales, route_idx, route_gate, activation,
+                  renormalize, capacity_factor, norm_pre, norm_post, norm_eps, n_shared, router_bias)
+    dbg, dptr = _debug(a, k, n_shared, norm_pre is not None, dev, debug, events)
+    rc = lib().grok_moe_forward_static(ctypes.byref(a), dptr, _stream(stream))
+    _raise(rc, "grok_moe_forward_static")
     return out, dbg
 
 

@@ -6,8 +6,16 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 using namespace gmoe;
 
+// Workspace of grok_moe_forward_static: one copy per device, held until the
+// process ends. Host code never uses this name as an address (on the host it
+// is only a stand-in for the symbol); the device address comes from
+// hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[GROK_MOE_STATIC_WORKSPACE_BYTES];
 
 namespace {
 
@@ -326,6 +334,38 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
   return GROK_MOE_OK;
 }
 
+// Device address of `scratch` on the current device, looked up on the first
+// call per device (with that device current) and kept.
+static int static_workspace(void** out) {
+  static std::mutex mu;
+  static std::atomic<void*> ptr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GROK_MOE_EHIP;
+  if (dev < 0 || dev >= 64) return GROK_MOE_EUNSUPPORTED;
+  void* p = ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GROK_MOE_EHIP;
+      ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return GROK_MOE_OK;
+}
+
+int grok_moe_forward_static(const grok_moe_args* a, const grok_moe_debug* dbg, void* stream) {
+  const int rc = validate(a);
+  if (rc != GROK_MOE_OK || a->T == 0) return rc;
+  const size_t need = make_plan(a->T, a->d, a->f, a->E, a->k, a->n_shared, a->act_dtype, a->w_dtype).total;
+  if (need > GROK_MOE_STATIC_WORKSPACE_BYTES) return GROK_MOE_EWORKSPACE;
+  void* ws = nullptr;
+  const int st = static_workspace(&ws);
+  if (st != GROK_MOE_OK) return st;
+  return grok_moe_forward_ex(a, ws, GROK_MOE_STATIC_WORKSPACE_BYTES, dbg, stream);
+}
+
 static int forward_alloc(const grok_moe_args* a, void* stream) {
   int rc = validate(a);
   if (rc != GROK_MOE_OK) return rc;
@@ -380,7 +420,9 @@ const char* grok_moe_status_string(int status) {
       return "unsupported shape (E <= 256 (64 for fp32), k <= 8, n_shared <= 4, d % 256 == 0, f % 256 == 0 for "
              "bf16/int8)";
     case GROK_MOE_EALIGN: return "misaligned pointer (16-byte tensors, 256-byte workspace)";
-    case GROK_MOE_EWORKSPACE: return "workspace missing or too small";
+    case GROK_MOE_EWORKSPACE:
+      return "workspace missing or too small (grok_moe_forward_static: the shape needs more than its static "
+             "workspace)";
     case GROK_MOE_EHIP: return "HIP runtime call failed";
   }
   return "unknown status";

@@ -227,6 +227,21 @@ def test_build_rejects_scratch_kernels():
     assert scratch_kernels(remarks) == [("_Z1bv", 336)]
 
 
+def test_static_workspace_holds_the_grok1_layer_up_to_128_tokens():
+    # the header's statement about GROK_MOE_STATIC_WORKSPACE_BYTES (64 MiB)
+    assert gm.STATIC_WORKSPACE_BYTES == 64 << 20
+    for wdt in (gm.BF16, gm.I8):
+        for T in (1, 8, 64, 65, 128):
+            assert 0 < gm.grok_moe_workspace_bytes(T, 6144, 32768, 8, 2, gm.BF16, wdt) <= gm.STATIC_WORKSPACE_BYTES
+
+
+def test_static_entry_point_validates_before_touching_a_gpu():
+    a = _args(T=8, d=256, f=256, E=8, k=9)
+    assert gm.lib().grok_moe_forward_static(ctypes.byref(a), None, None) == gm.EINVAL
+    a = _args(T=0, d=256, f=256, E=8, k=2)
+    assert gm.lib().grok_moe_forward_static(ctypes.byref(a), None, None) == gm.OK
+
+
 def _cpu_layer(T=4, d=64, f=128, E=4, wdt="bf16"):
     torch = pytest.importorskip("torch")
     adt = torch.float32 if wdt == "f32" else torch.bfloat16
