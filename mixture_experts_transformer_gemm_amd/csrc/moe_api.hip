@@ -36,6 +36,7 @@ struct Plan {
   int gsplits = 1; // split-K factor of the streaming gate/up projection
   int bm = 256;    // tiled path: rows per workgroup tile
   int rsplits = 0; // split-K factor of the many-expert router GEMM (0: fused router)
+  int pp = 0;      // tiled path: the ping-pong kernel (bf16 weights, 256-row tiles)
   int64_t rows_cap = 0;
   size_t off_idx = 0, off_gate = 0, off_counts = 0, off_offsets = 0, off_perm = 0, off_pos = 0, off_pblk = 0;
   size_t off_tiles = 0;
@@ -105,9 +106,18 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
     p.bm = r <= 32 ? 64 : (r <= 96 ? 128 : 256);
     // past 256 rows an expert's last 256-row tile is mostly empty yet streams
     // its whole weight tile; 320-row tiles (bf16) need fewer row tiles
-    // (measured: 15% off the gate/up + down time at 287 rows per expert, 4%
-    // at 512, level at 2048)
+    // (measured: 15% off the gate/up + down time at 287 rows per expert)
     if (wdt == GROK_MOE_BF16 && r > 256) p.bm = 320;
+    // from 512 rows per expert on, bf16 weights run the ping-pong kernel
+    // (256-row tiles; measured: Grok-1 prefill layer 18.4 against 19.3-20.5
+    // ms, Mixtral 8x22B prefill 9.4 against 9.9 ms, the skewed 2048-token
+    // layer 5.4 against 6.0 ms); below, an expert's second 256-row tile is
+    // mostly empty (the 256-expert prefill, about 287 rows per expert: 9.6
+    // against 9.1 ms with 320-row tiles)
+    if (wdt == GROK_MOE_BF16 && r >= 512) {
+      p.bm = 256;
+      p.pp = 1;
+    }
     // 8-bit weights: 128-row tiles up to about 384 rows per expert (their
     // LDS stages are smaller, so the 4-wavefront tile keeps more in flight)
     if (wdt == GROK_MOE_I8 && r <= 384) p.bm = 128;
@@ -124,7 +134,16 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
     const int64_t exp_tiles =
         ((int64_t)E * ((T * k / E + p.bm - 1) / p.bm) + (int64_t)ns * ((T + p.bm - 1) / p.bm)) * (d / 256);
     const int64_t last = exp_tiles % 256;
-    if (s == 1 && last > 0 && last <= 128 && (f / 2) % 64 == 0) s = 2;
+    if (!p.pp && s == 1 && last > 0 && last <= 128 && (f / 2) % 64 == 0) s = 2;
+    if (p.pp && s == 1 && (f / 2) % 64 == 0) {
+      // ping-pong down tiles: an expert's last row tile is on average half
+      // full, so about E (r / 256 + 1/2) row tiles run; two splits when that
+      // leaves the last of fewer than 32 rounds at most three quarters full
+      const double rt = (double)E * ((double)T * k / E / 256.0 + 0.5) + (double)ns * ((double)T / 256.0 + 0.5);
+      const double rounds = rt * (double)(d / 256) / 256.0;
+      const double frac = rounds - floor(rounds);
+      if (rounds < 32.0 && frac > 0.0 && frac <= 0.75) s = 2;
+    }
     p.splits = s;
   }
   if (E > kFusedRouterE) {
@@ -299,8 +318,12 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
     GMOE_TRY(launch_stream_gateup(w8, p.mt_max, p.gsplits, (const bf16_bits*)A, rv, a->w_gate, a->w_up, a->scales, T,
                                   p.rows_cap, d, f, E, act, (bf16_bits*)H, (float*)(w + p.off_G), st));
   } else {
-    GMOE_TRY(launch_tiled_gateup(w8, p.bm, (const bf16_bits*)A, rv, a->w_gate, a->w_up, a->scales, T, p.rows_cap, d,
-                                 f, E, act, (bf16_bits*)H, st));
+    if (p.pp)
+      GMOE_TRY(launch_pp_gateup((const bf16_bits*)A, rv, (const bf16_bits*)a->w_gate, (const bf16_bits*)a->w_up, T,
+                                p.rows_cap, d, f, E, act, (bf16_bits*)H, st));
+    else
+      GMOE_TRY(launch_tiled_gateup(w8, p.bm, (const bf16_bits*)A, rv, a->w_gate, a->w_up, a->scales, T, p.rows_cap,
+                                   d, f, E, act, (bf16_bits*)H, st));
   }
   // stage 3: down projection
   if (!record(dbg, 3, st)) return GROK_MOE_EHIP;
@@ -310,8 +333,12 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
     GMOE_TRY(launch_stream_down(w8, p.mt_max, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d,
                                 f, E, Y, st));
   } else {
-    GMOE_TRY(launch_tiled_down(w8, p.bm, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d, f,
-                               E, Y, st));
+    if (p.pp)
+      GMOE_TRY(launch_pp_down(p.splits, (const bf16_bits*)H, rv, (const bf16_bits*)a->w_down, p.rows_cap, d, f, E, Y,
+                              st));
+    else
+      GMOE_TRY(launch_tiled_down(w8, p.bm, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d, f,
+                                 E, Y, st));
   }
   // stage 4: gate-weighted combine
   if (!record(dbg, 4, st)) return GROK_MOE_EHIP;

@@ -89,4 +89,7 @@ __device__ __forceinline__ int rslot(int r, int c) { return c ^ (r & 7) ^ ((r >>
 // s_waitcnt vmcnt(n), other counters left alone
 #define GMOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
+// s_waitcnt with vmcnt(n) and lgkmcnt(0) (expcnt left at its maximum)
+#define GMOE_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (((n) >> 4) << 14))
+
 }  // namespace gmoe

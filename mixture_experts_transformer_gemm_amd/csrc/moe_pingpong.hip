@@ -1,0 +1,362 @@
+// Ping-pong grouped GEMM of the Grok-1 MoE layer for gfx950 (MI355X): the
+// large-batch (prefill) gate/up and down projections with bf16 weights.
+//
+// Each expert is one segment of a grouped GEMM over the expert-contiguous row
+// permutation (Grok-1 book ch. 11, section 11.3.1: sparse reorder + grouped
+// GEMM). Gate/up pass: H = act(X Wg^T) * (X Wu^T) -> bf16 (field guide, "MoE
+// 子层": two input projections, GELU on one, elementwise product). Down pass:
+// Y = H Wd^T -> fp32 partial sums.
+//
+// Workgroup tile: 256 rows x 256 weight rows, 8 wavefronts, two per SIMD
+// (256 x 256 fp32 accumulators fill half of each SIMD's register file). The
+// reduction runs in slices of 64 values; both operands of a slice reach LDS
+// by global_load_lds_dwordx4, each load instruction fetching 8 whole 128-byte
+// lines (8 rows x 64 values: fetching half lines, a slice of 32 values,
+// measured slower, since the other half of every line is evicted from the
+// vector L1 before the next slice asks for it). LDS holds three activation
+// slices and two weight slices (160 KB): the activation rows, gathered token
+// rows that mostly miss L2, are loaded two slices ahead, the weights one.
+//
+// The two wavefronts of a SIMD take turns (a ping-pong): wavefronts 0-3
+// (group 0) and 4-7 (group 1) run the same loop one phase apart, and between
+// two workgroup barriers one group only issues MFMAs on fragments it already
+// holds in registers while the other group reads the next fragments from LDS
+// and issues global loads. Each SIMD's matrix core is thus fed by one
+// wavefront while its partner waits on memory (measured with the operands
+// held in registers, this barrier pattern keeps the matrix cores 99% busy).
+// A slice is read in four memory phases (half 0 and half 1 of its
+// reduction values, by group 0 and then group 1); group 0 loads the
+// activation half of every slice, group 1 the weight half, and the barrier
+// that ends a slice's last phase follows every wavefront's wait (vmcnt) for
+// its own loads of the next slice.
+//
+// Wavefront (s, g), s = SIMD (wavefront mod 4; wavefronts w and w + 4 share a
+// SIMD on gfx950), g = group: rows 32 s .. 32 s + 31 and 128 + 32 s .. 128 +
+// 32 s + 31 of the tile (so a partly filled tile spreads its rows over all
+// four SIMDs); weight rows: the gate/up pass pairs gate channels 64 g .. 64 g
+// + 63 with the same up channels (LDS rows 0-127 gate, 128-255 up), the down
+// pass takes output channels 128 g .. 128 g + 127. Products use
+// v_mfma_f32_32x32x16_bf16 with the weight fragment as "A" and the activation
+// fragment as "B": lane l supplies row (l mod 32) and 8 reduction values of
+// half l / 32; result register v of lane l is C[8 (v / 4) + 4 (l / 32) +
+// (v mod 4)][l mod 32] (channel, row).
+//
+// Tile order: the tiles that exist are numbered expert by expert; within an
+// expert, groups of 4 row tiles are walked channel tile by channel tile with
+// the row tiles fastest; the numbering is split into 8 contiguous ranges, one
+// per XCD (workgroup i runs on XCD i mod 8), so the 32 workgroups resident on
+// an XCD share 4 row tiles of activations and 8 weight tiles through its L2.
+//
+// What bounds it (Grok-1 prefill, measured): with no global loads in the loop
+// the gate/up pass runs at 64% of the bf16 peak and the down pass at 75%; the
+// loads alone (almost no MFMAs) take about as long as the MFMAs alone, and the
+// two overlap only in part. The waits for loads are a few percent of the
+// loop: the limit is the rate at which the memory system delivers the 64 KB
+// of a slice (L2 hit rate about 55%), and with random bf16 operands the chip
+// also holds a lower clock under full MFMA load.
+#include "moe_device.h"
+
+#include <type_traits>
+
+namespace gmoe {
+
+namespace {
+
+constexpr int kPM = 256;          // rows per tile
+constexpr int kPN = 256;          // weight rows per tile
+constexpr int kPK = 64;           // reduction values per slice
+constexpr int kPRow = kPK * 2;    // LDS bytes per row and slice: one 128-byte line
+constexpr int kPSliceA = kPM * kPRow;  // activation half of a slice: 32 KB
+constexpr int kPSliceW = kPN * kPRow;  // weight half: 32 KB
+// Row tiles per tile group: 32 workgroups resident on one XCD then hold 4
+// row tiles x 8 channel tiles of one expert (measured at the Grok-1 prefill:
+// layer 18.6 ms against 19.3 ms walking all of an expert's row tiles per
+// channel tile, 19.1 with groups of 2 or 3, 18.8 with 5 or 8)
+constexpr int kPGroup = 4;
+// LDS: three activation buffers, then two weight buffers (160 KB)
+constexpr int kPWOff = 3 * kPSliceA;
+constexpr int kPLds = kPWOff + 2 * kPSliceW;
+
+struct PTile {
+  int e, m0, M, n0;
+};
+
+// slot of 16-byte chunk c of LDS row R (8 chunks): conflict-free for fragment
+// reads of 32 rows at two chunks and for the 1 KB load writes (8 rows)
+__device__ __forceinline__ int pslot(int R, int c) { return c ^ (R & 7) ^ ((R >> 3) & 1); }
+
+// This workgroup's tile, or false when it has none. Output channels per tile:
+// 128 (gate/up: 128 gate + the same 128 up weight rows) or 256 (down).
+template <bool GATEUP>
+__device__ __forceinline__ bool pp_select(const RouteView& rv, int E, int N, PTile& t) {
+  constexpr int kCh = GATEUP ? kPN / 2 : kPN;
+  const int nN = N / kCh;
+  const int mtiles = rv.tile_off[E];
+  const int total = mtiles * nN;
+  const int per_xcd = (total + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  if (slot >= per_xcd) return false;
+  const int L = (blockIdx.x & 7) * per_xcd + slot;
+  if (L >= total) return false;
+  // expert e's tiles are [tile_off[e] nN, tile_off[e+1] nN), so L / nN is one
+  // of e's row tiles
+  const int e = rv.tile_e[L / nN];
+  const int mt0 = rv.tile_off[e];
+  const int mte = rv.tile_off[e + 1] - mt0;
+  // within the expert: groups of kPGroup row tiles, each walked channel tile
+  // by channel tile with its row tiles fastest (the last group may be smaller)
+  const int within = L - mt0 * nN;
+  const int gfull = mte / kPGroup;
+  int nt, mrow;
+  if (within < gfull * kPGroup * nN) {
+    const int gi = within / (kPGroup * nN), rem = within - gi * kPGroup * nN;
+    nt = rem / kPGroup;
+    mrow = gi * kPGroup + (rem - nt * kPGroup);
+  } else {
+    const int gl = mte - gfull * kPGroup, rem = within - gfull * kPGroup * nN;
+    nt = rem / gl;
+    mrow = gfull * kPGroup + (rem - nt * gl);
+  }
+  const int mloc = mrow * kPM;
+  t.e = e;
+  t.m0 = rv.offsets[e] + mloc;
+  t.M = min(kPM, rv.counts[e] - mloc);
+  t.n0 = nt * kCh;
+  return true;
+}
+
+}  // namespace
+
+// A: x (gate/up, rows gathered through perm) or H (down, contiguous rows);
+// w0, w1: gate and up weights (gate/up) or the down weights (both); K: the
+// reduction length (d or f), N: output channels of the weight matrices (f or
+// d); out: H (bf16) or Y (fp32, gridDim.y partial sums over equal slices of
+// the reduction).
+template <bool GATEUP>
+__global__ __launch_bounds__(512, 1) void pp_kernel(const bf16_bits* __restrict__ A, RouteView rv,
+                                                    const bf16_bits* __restrict__ w0,
+                                                    const bf16_bits* __restrict__ w1, int64_t T, int K, int N,
+                                                    int E, int64_t rows_cap, int act, void* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  PTile t;
+  if (!pp_select<GATEUP>(rv, E, N, t)) return;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int s = wave & 3, g = wave >> 2;
+  const int r32 = lane & 31, hg = lane >> 5;
+  const int S = gridDim.y, sp = blockIdx.y;
+  const int kspan = K / S, kbeg = sp * kspan;
+  const int nsl = kspan / kPK;  // slices
+
+  // Sources of this lane's 8 load instructions per slice (slice 0): group 0
+  // fills the activation half (instruction q writes LDS rows 8 (8 s + q) ..
+  // + 7), group 1 the weight half. Lane l of an instruction writes row
+  // 8 I + l / 8 at slot l mod 8, so it reads the chunk stored there; the 8
+  // lanes of a row fetch one whole 128-byte line.
+  const char* src[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int I = 8 * s + q;
+    const int R = 8 * I + (lane >> 3);
+    const int c = pslot(R, lane & 7);
+    const bf16_bits* row;
+    if (g == 0) {
+      const int r = R < t.M ? R : t.M - 1;  // rows past the segment's end repeat its last row
+      if (GATEUP) {
+        int tok = rv.perm[t.m0 + r];
+        tok = tok < 0 ? 0 : (tok >= T ? (int)(T - 1) : tok);
+        row = A + (int64_t)tok * K;
+      } else {
+        row = A + (int64_t)(t.m0 + r) * K;
+      }
+    } else if (GATEUP) {
+      row = (R < kPN / 2 ? w0 : w1) + ((int64_t)t.e * N + t.n0 + (R & (kPN / 2 - 1))) * K;
+    } else {
+      row = w0 + ((int64_t)t.e * N + t.n0 + R) * K;
+    }
+    src[q] = (const char*)(row + kbeg) + c * 16;
+  }
+  // activation slice sl lives in buffer sl mod 3, weight slice sl in buffer sl mod 2
+  auto issue = [&](int sl) {
+    char* dst = lds + (g == 0 ? (sl % 3) * kPSliceA : kPWOff + (sl & 1) * kPSliceW) + 8 * s * 1024;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dma16_policy<0>(src[q] + (size_t)sl * kPRow, dst + q * 1024);
+  };
+
+  // fragments of half h (32 reduction values) of one slice: 4 weight tiles
+  // x 2 steps, 2 row tiles x 2 steps
+  u32x4 fw[2][4], fx[2][2];
+  auto read_frags = [&](int sl, int h) {
+    const char* ba = lds + (sl % 3) * kPSliceA;
+    const char* bw = lds + kPWOff + (sl & 1) * kPSliceW;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int c = 4 * h + 2 * st + hg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int R = (GATEUP ? (i < 2 ? 0 : kPN / 2) + 64 * g + 32 * (i & 1) : 128 * g + 32 * i) + r32;
+        fw[st][i] = *reinterpret_cast<const u32x4*>(bw + R * kPRow + pslot(R, c) * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int R = 32 * (s + 4 * j) + r32;
+        fx[st][j] = *reinterpret_cast<const u32x4*>(ba + R * kPRow + pslot(R, c) * 16);
+      }
+    }
+  };
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  // row tiles of this wavefront that hold rows of the segment (0, 1 or 2):
+  // the others get no MFMAs (loads and barriers are the same for all)
+  const int jv = (32 * s < t.M ? 1 : 0) + (128 + 32 * s < t.M ? 1 : 0);
+  auto mfmas = [&](auto jv_tag) {
+    constexpr int JV = decltype(jv_tag)::value;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < JV; ++j) acc[i][j] = mfma32(fw[st][i], fx[st][j], acc[i][j]);
+  };
+  // a workgroup barrier that no instruction crosses in either direction
+  auto phase_end = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Phases: slice sl is read in four memory phases, half 0 then half 1 by
+  // group 0 (phases 4 sl, 4 sl + 2) and by group 1 one phase later, so its
+  // buffers are free from phase 4 sl + 4 on. Group 0 loads the activation
+  // rows two slices ahead (slice sl + 2 in phase 4 sl, into the buffer slice
+  // sl - 1 used), group 1 the weights one slice ahead (slice sl + 2 at the end
+  // of phase 4 sl + 3, after its own last reads of slice sl). Both wait for
+  // their loads of slice sl + 1 at the end of phase 4 sl + 3; a wavefront's
+  // loads land in issue order, so group 0 waits for all but the newest 8.
+  auto run = [&](auto jv_tag) {
+    issue(0);
+    if (nsl > 1) issue(1);
+    if (nsl > 1)
+      GMOE_WAIT_VM(8);
+    else
+      GMOE_WAIT_VM(0);
+    phase_end();
+    if (g == 0) {
+      for (int sl = 0; sl < nsl; ++sl) {
+        read_frags(sl, 0);
+        if (sl + 2 < nsl) issue(sl + 2);
+        phase_end();
+        mfmas(jv_tag);
+        phase_end();
+        read_frags(sl, 1);
+        phase_end();
+        mfmas(jv_tag);
+        __builtin_amdgcn_sched_barrier(0);
+        if (sl + 2 < nsl)
+          GMOE_WAIT_VM(8);
+        else
+          GMOE_WAIT_VM(0);
+        phase_end();
+      }
+      phase_end();  // group 1's last compute phase
+    } else {
+      phase_end();  // group 0's first memory phase
+      for (int sl = 0; sl < nsl; ++sl) {
+        read_frags(sl, 0);
+        phase_end();
+        mfmas(jv_tag);
+        phase_end();
+        read_frags(sl, 1);
+        GMOE_WAIT_VM_LGKM0(0);
+        if (sl + 2 < nsl) issue(sl + 2);
+        phase_end();
+        mfmas(jv_tag);
+        phase_end();
+      }
+    }
+  };
+  if (jv == 2)
+    run(std::integral_constant<int, 2>{});
+  else if (jv == 1)
+    run(std::integral_constant<int, 1>{});
+  else
+    run(std::integral_constant<int, 0>{});
+
+  // epilogue: this lane's rows 32 (s + 4 j) + r32 of the tile
+  if (GATEUP) {
+    bf16_bits* H = (bf16_bits*)out;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int m = 32 * (s + 4 * j) + r32;
+      if (m < t.M) {
+        bf16_bits* hrow = H + (int64_t)(t.m0 + m) * N + t.n0 + 64 * g;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float h[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) h[v] = glu_act(act, acc[i][j][4 * q + v]) * acc[i + 2][j][4 * q + v];
+            uint2 o;
+            o.x = pack_bf16x2(h[0], h[1]);
+            o.y = pack_bf16x2(h[2], h[3]);
+            *reinterpret_cast<uint2*>(hrow + 32 * i + 8 * q + 4 * hg) = o;
+          }
+      }
+    }
+  } else {
+    float* Y = (float*)out + (int64_t)sp * rows_cap * N;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int m = 32 * (s + 4 * j) + r32;
+      if (m < t.M) {
+        float* yrow = Y + (int64_t)(t.m0 + m) * N + t.n0 + 128 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(yrow + 32 * i + 8 * q + 4 * hg) =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+      }
+    }
+  }
+}
+
+namespace {
+
+
+template <bool GATEUP>
+hipError_t pp_launch(hipStream_t st, const bf16_bits* A, RouteView rv, const bf16_bits* w0, const bf16_bits* w1,
+                     int64_t T, int64_t rows_cap, int K, int N, int E, int splits, int act, void* out) {
+  constexpr int lds = kPLds;
+  static std::atomic<unsigned long long> lds_set{0};
+  const hipError_t attr = set_lds_limit(reinterpret_cast<const void*>(&pp_kernel<GATEUP>), lds, lds_set);
+  if (attr != hipSuccess) return attr;
+  // grid: an upper bound of the tiles (sum over experts of ceil(rows_e / 256)
+  // <= rows / 256 + E), times the channel tiles, rounded up to a multiple of 8
+  const int nN = N / (GATEUP ? kPN / 2 : kPN);
+  const int64_t tiles = (rows_cap / kPM + E) * nN;
+  const dim3 grid((unsigned)((tiles + 7) / 8 * 8), (unsigned)splits);
+  hipLaunchKernelGGL((pp_kernel<GATEUP>), grid, dim3(512), lds, st, A, rv, w0, w1, T, K, N, E, rows_cap, act,
+                     out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pp_gateup(const bf16_bits* x, RouteView rv, const bf16_bits* wg, const bf16_bits* wu, int64_t T,
+                            int64_t rows_cap, int d, int f, int E, int act, bf16_bits* H, hipStream_t st) {
+  return pp_launch<true>(st, x, rv, wg, wu, T, rows_cap, d, f, E, 1, act, H);
+}
+
+hipError_t launch_pp_down(int splits, const bf16_bits* H, RouteView rv, const bf16_bits* wd, int64_t rows_cap, int d,
+                          int f, int E, float* Y, hipStream_t st) {
+  return pp_launch<false>(st, H, rv, wd, wd, rows_cap, rows_cap, f, d, E, splits, 0, Y);
+}
+
+}  // namespace gmoe

@@ -238,8 +238,6 @@ __device__ __forceinline__ void dma16(const void* src, char* lds_base) {
 #endif
 }
 
-// s_waitcnt with vmcnt(n) and lgkmcnt(0) (expcnt left at its maximum)
-#define GMOE_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (((n) >> 4) << 14))
 
 template <int BM, bool GATEUP, int NW, int NS, bool W8>
 __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __restrict__ A, RouteView rv,

@@ -45,7 +45,8 @@ def test_bf16_layer_small(T):
     _full_check(w)
 
 
-@pytest.mark.parametrize("T,d,f", [(3, 512, 256), (48, 512, 768), (200, 512, 768), (300, 768, 1280), (600, 256, 256)])
+@pytest.mark.parametrize("T,d,f", [(3, 512, 256), (48, 512, 768), (200, 512, 768), (300, 768, 1280), (600, 256, 256),
+                                   (1500, 512, 768), (2600, 768, 1280)])
 def test_bf16_layer_other_shapes(T, d, f):
     w = synthetic.make("decode", T=T, d=d, f=f, seed=100 + T)
     _full_check(w)
@@ -235,13 +236,17 @@ def test_permutation_many_blocks(E, k, cf):
     assert normwise_err(got[toks], ref) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("w_dtype", ["bf16", "i8"])
-def test_tile_boundaries_and_empty_experts(w_dtype):
-    # 1,100 tokens at top-2 average 275 rows per expert, so bf16 weights run 320-row tiles (8-bit: 128-row):
-    # segments of 0, 1, 319, 320, 321, 640, 599 and 0 rows put tile edges on both sides of every boundary
-    # and leave the first and last experts empty (tile table entries must skip them)
-    T, E, k = 1100, 8, 2
-    sizes = [0, 1, 319, 320, 321, 640, 599, 0]
+@pytest.mark.parametrize("w_dtype,T,sizes", [("bf16", 1100, [0, 1, 319, 320, 321, 640, 599, 0]),
+                                              ("bf16", 1100, [0, 255, 256, 257, 512, 513, 1, 406]),
+                                              ("bf16", 2100, [0, 255, 256, 257, 1024, 1025, 1, 1382]),
+                                              ("i8", 1100, [0, 1, 319, 320, 321, 640, 599, 0])])
+def test_tile_boundaries_and_empty_experts(w_dtype, T, sizes):
+    # 1,100 tokens at top-2 average 275 rows per expert, so bf16 weights run 320-row tiles (8-bit: 128-row);
+    # 2,100 tokens average 525, which runs the 256-row ping-pong tiles. Segments of 0, 1, 255 .. 257,
+    # 319 .. 321, 512, 513, 640, 1024 and 1025 rows put tile edges on both sides of every boundary, and
+    # empty first and last experts must be skipped by the tile table
+    E, k = 8, 2
+    assert sum(sizes) == T * k
     labels = np.repeat(np.arange(E, dtype=np.int32), sizes)            # sorted by expert, 2T long
     idx = np.stack([labels[:T], labels[T:]], axis=1)                   # runs < T long: distinct per token
     assert np.all(idx[:, 0] != idx[:, 1])
