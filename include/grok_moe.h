@@ -31,6 +31,13 @@
  *      w_down    [E][d][f]      row i of expert e = the f weights of output i
  *      scales    fp32, [gate: E*f | up: E*f | down: E*d]; 8-bit weights only;
  *                the weight is q * scale of its output channel
+ *    The weight layouts are the transposes of the [in][out] matrices the pages
+ *    write (router [d][E], input projections [E][d][f], down projection
+ *    [E][f][d]): every weight row holds one output channel's reduction values
+ *    contiguously, which is what the matrix-core operands take (8 consecutive
+ *    reduction values per lane) and what lets the decode kernels stream each
+ *    weight row as whole 128-byte lines. A caller holding [in][out] matrices
+ *    transposes them once, at load time.
  *  - Asynchronous: a return of GROK_MOE_OK means the work is enqueued on
  *    `stream` (a hipStream_t; NULL is the default stream). Nothing is
  *    synchronised and nothing is copied to the host; device faults surface at
@@ -41,8 +48,8 @@
  *  - `out` must not alias any input. T = 0 is a no-op that returns OK.
  *  - Supported shapes (GROK_MOE_EUNSUPPORTED otherwise): 1 <= k <= min(E, 8),
  *    E <= 256 routed experts (E <= 64 with fp32 activations), at most 4
- *    shared experts; bf16 and 8-bit weights need d % 256 == 0 and
- *    f % 256 == 0; fp32 needs d % 8 == 0 and f % 4 == 0; T <= 2^20.
+ *    shared experts; bf16 and 8-bit weights need d % 64 == 0 and
+ *    f % 128 == 0; fp32 needs d % 8 == 0 and f % 4 == 0; T <= 2^20.
  *  - Pointers must be 16-byte aligned (GROK_MOE_EALIGN otherwise).
  *  - Thread-safe: the only global state is each kernel's LDS limit, set
  *    once per device on first use. Concurrent calls on different streams

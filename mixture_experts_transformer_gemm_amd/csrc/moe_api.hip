@@ -56,7 +56,7 @@ int check_shape(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t n
   if (act == GROK_MOE_F32) {
     if (d % 8 || f % 4) return GROK_MOE_EUNSUPPORTED;
   } else {
-    if (d % 256 || f % 256) return GROK_MOE_EUNSUPPORTED;
+    if (d % 64 || f % 128) return GROK_MOE_EUNSUPPORTED;
   }
   return GROK_MOE_OK;
 }
@@ -69,7 +69,9 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
   p.rows_cap = T * K;
   if (act == GROK_MOE_F32) {
     p.path = PATH_F32;
-  } else if ((wdt == GROK_MOE_BF16 && T <= kStreamMaxT) || (wdt == GROK_MOE_I8 && T <= kStream8MaxT)) {
+  } else if ((wdt == GROK_MOE_BF16 && T <= kStreamMaxT) || (wdt == GROK_MOE_I8 && T <= kStream8MaxT && d % 128 == 0)) {
+    // (8-bit weights stream in stages of 128 reduction values, so d % 128;
+    // other widths take the tiled path, whose stages are 64 values)
     p.path = PATH_STREAM;
     p.mt_max = (int)T;  // rows of one expert <= T
     // enough workgroups for the down projection, about 3 per CU (measured
@@ -81,7 +83,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
     const int64_t ks = wdt == GROK_MOE_I8 ? 128 : 64;
     const int64_t ch_per_wg = wdt == GROK_MOE_I8 ? 256 : 128;
     int s = 1;
-    while (s < 8 && (int64_t)Et * (d / ch_per_wg) * s < 512 && (f / (2 * s)) % ks == 0) s *= 2;
+    while (s < 8 && (int64_t)Et * ((d + ch_per_wg - 1) / ch_per_wg) * s < 512 && (f / (2 * s)) % ks == 0) s *= 2;
     p.splits = s;
     // Fine-grained layers (64 or more routed experts, bf16 weights): each
     // expert has few gate/up workgroups (f / 64) and the count that runs
@@ -123,7 +125,8 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
     if (wdt == GROK_MOE_I8 && r <= 384) p.bm = 128;
     // split the down projection's reduction while its tiles alone would
     // leave CUs idle: (row tiles upper bound) x (d / 256) tiles per split
-    const int64_t tiles = (p.rows_cap / p.bm + Et) * (d / 256);
+    const int64_t dtiles = (d + 255) / 256;  // down channel tiles (the last may be partial)
+    const int64_t tiles = (p.rows_cap / p.bm + Et) * dtiles;
     int s = 1;
     while (s < 8 && tiles * s < 1024 && (f / (2 * s)) % 64 == 0) s *= 2;
     // The down tiles run one workgroup per CU (256 CUs). When the tiles
@@ -132,7 +135,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
     // (measured at 8,192 tokens, 1,344 tiles = 5.25 rounds: down 6.8 ->
     // 6.5 ms; at 16,384 tokens, 9.75 rounds, splitting is 3% slower)
     const int64_t exp_tiles =
-        ((int64_t)E * ((T * k / E + p.bm - 1) / p.bm) + (int64_t)ns * ((T + p.bm - 1) / p.bm)) * (d / 256);
+        ((int64_t)E * ((T * k / E + p.bm - 1) / p.bm) + (int64_t)ns * ((T + p.bm - 1) / p.bm)) * dtiles;
     const int64_t last = exp_tiles % 256;
     if (!p.pp && s == 1 && last > 0 && last <= 128 && (f / 2) % 64 == 0) s = 2;
     if (p.pp && s == 1 && (f / 2) % 64 == 0) {
@@ -140,7 +143,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
       // full, so about E (r / 256 + 1/2) row tiles run; two splits when that
       // leaves the last of fewer than 32 rounds at most three quarters full
       const double rt = (double)E * ((double)T * k / E / 256.0 + 0.5) + (double)ns * ((double)T / 256.0 + 0.5);
-      const double rounds = rt * (double)(d / 256) / 256.0;
+      const double rounds = rt * (double)dtiles / 256.0;
       const double frac = rounds - floor(rounds);
       if (rounds < 32.0 && frac > 0.0 && frac <= 0.75) s = 2;
     }
@@ -444,8 +447,8 @@ const char* grok_moe_status_string(int status) {
     case GROK_MOE_OK: return "ok";
     case GROK_MOE_EINVAL: return "invalid argument (null pointer, negative size, k > E or bad dtype)";
     case GROK_MOE_EUNSUPPORTED:
-      return "unsupported shape (E <= 256 (64 for fp32), k <= 8, n_shared <= 4, d % 256 == 0, f % 256 == 0 for "
-             "bf16/int8)";
+      return "unsupported shape (E <= 256 (64 for fp32), k <= 8, n_shared <= 4, d % 64 == 0, f % 128 == 0 for "
+             "bf16/int8, d % 8 == 0, f % 4 == 0 for fp32)";
     case GROK_MOE_EALIGN: return "misaligned pointer (16-byte tensors, 256-byte workspace)";
     case GROK_MOE_EWORKSPACE:
       return "workspace missing or too small (grok_moe_forward_static: the shape needs more than its static "

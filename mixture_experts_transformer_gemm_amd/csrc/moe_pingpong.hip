@@ -90,7 +90,7 @@ __device__ __forceinline__ int pslot(int R, int c) { return c ^ (R & 7) ^ ((R >>
 template <bool GATEUP>
 __device__ __forceinline__ bool pp_select(const RouteView& rv, int E, int N, PTile& t) {
   constexpr int kCh = GATEUP ? kPN / 2 : kPN;
-  const int nN = N / kCh;
+  const int nN = (N + kCh - 1) / kCh;  // the last channel tile may reach past N
   const int mtiles = rv.tile_off[E];
   const int total = mtiles * nN;
   const int per_xcd = (total + 7) >> 3;
@@ -172,7 +172,8 @@ __global__ __launch_bounds__(512, 1) void pp_kernel(const bf16_bits* __restrict_
     } else if (GATEUP) {
       row = (R < kPN / 2 ? w0 : w1) + ((int64_t)t.e * N + t.n0 + (R & (kPN / 2 - 1))) * K;
     } else {
-      row = w0 + ((int64_t)t.e * N + t.n0 + R) * K;
+      // rows past the last output channel read the last one (not stored)
+      row = w0 + ((int64_t)t.e * N + min(t.n0 + R, N - 1)) * K;
     }
     src[q] = (const char*)(row + kbeg) + c * 16;
   }
@@ -316,12 +317,15 @@ __global__ __launch_bounds__(512, 1) void pp_kernel(const bf16_bits* __restrict_
       const int m = 32 * (s + 4 * j) + r32;
       if (m < t.M) {
         float* yrow = Y + (int64_t)(t.m0 + m) * N + t.n0 + 128 * g;
+        const int nleft = N - t.n0 - 128 * g;  // channels of this wavefront inside N (a multiple of 64)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
+          if (32 * i < nleft) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<float4*>(yrow + 32 * i + 8 * q + 4 * hg) =
-                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<float4*>(yrow + 32 * i + 8 * q + 4 * hg) =
+                  make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          }
       }
     }
   }
@@ -339,7 +343,8 @@ hipError_t pp_launch(hipStream_t st, const bf16_bits* A, RouteView rv, const bf1
   if (attr != hipSuccess) return attr;
   // grid: an upper bound of the tiles (sum over experts of ceil(rows_e / 256)
   // <= rows / 256 + E), times the channel tiles, rounded up to a multiple of 8
-  const int nN = N / (GATEUP ? kPN / 2 : kPN);
+  constexpr int kCh = GATEUP ? kPN / 2 : kPN;
+  const int nN = (N + kCh - 1) / kCh;
   const int64_t tiles = (rows_cap / kPM + E) * nN;
   const dim3 grid((unsigned)((tiles + 7) / 8 * 8), (unsigned)splits);
   hipLaunchKernelGGL((pp_kernel<GATEUP>), grid, dim3(512), lds, st, A, rv, w0, w1, T, K, N, E, rows_cap, act,

@@ -122,7 +122,9 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int kChW = (GATEUP ? 8 : 16) * WT;  // output channels per wavefront
-  const int nblk = N / (kBW * kChW);
+  // workgroups per expert; the last one may reach past N (the down pass with
+  // d % 128 != 0): its wavefronts past N read clamped weight rows, store nothing
+  const int nblk = (N + kBW * kChW - 1) / (kBW * kChW);
   const int e = blockIdx.x / nblk;
   const int nb = blockIdx.x - e * nblk;
   const int M = rv.counts[e];
@@ -150,9 +152,9 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
     const int c = rslot(R, lane & 7);
     const char* row;
     if (GATEUP)
-      row = (const char*)((r & 8) == 0 ? w0 : w1) + ((int64_t)e * N + c0 + 8 * (r >> 4) + (r & 7)) * K * wsz;
+      row = (const char*)((r & 8) == 0 ? w0 : w1) + ((int64_t)e * N + min(c0 + 8 * (r >> 4) + (r & 7), N - 1)) * K * wsz;
     else
-      row = (const char*)w0 + ((int64_t)e * N + c0 + r) * K * wsz;
+      row = (const char*)w0 + ((int64_t)e * N + min(c0 + r, N - 1)) * K * wsz;
     wsrc[q] = row + kbeg * wsz + c * 16;
   }
   const char* asrc[C::kQA];
@@ -292,6 +294,7 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
   for (int w = 0; w < WT; ++w) {
     // weight tile w: gate/up channels cw..cw+7, or down channels cw..cw+15
     const int cw = c0 + (GATEUP ? 8 : 16) * w;
+    if (cw >= N) continue;  // past the last channel (N is a multiple of 16)
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
       if (j < mv) {
@@ -352,7 +355,8 @@ static hipError_t stream_launch(unsigned gz, unsigned gy, hipStream_t st, const 
       set_lds_limit(reinterpret_cast<const void*>(&stream_kernel<GATEUP, MT, W8, WT>), lds, lds_set);
   if (attr != hipSuccess) return attr;
   // one workgroup per (expert, 8 wavefronts x channels per wavefront)
-  const unsigned gx = (unsigned)E * (unsigned)(N / (kBW * (GATEUP ? 8 : 16) * WT));
+  constexpr int kWgCh = kBW * (GATEUP ? 8 : 16) * WT;
+  const unsigned gx = (unsigned)E * (unsigned)((N + kWgCh - 1) / kWgCh);
   hipLaunchKernelGGL((stream_kernel<GATEUP, MT, W8, WT>), dim3(gx, gy, gz), dim3(kBW * 64), lds, st, A, rv, w0, w1,
                      scales, T, K, N, E, rows_cap, act, out);
   return hipGetLastError();

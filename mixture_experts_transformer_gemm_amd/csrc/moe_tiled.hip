@@ -64,7 +64,7 @@ using AccT = f32x16[TileCfg<BM, NW>::TI][TileCfg<BM, NW>::TJ];
 template <int BM, bool GATEUP>
 __device__ __forceinline__ bool select_tile(const RouteView& rv, int E, int N, Tile& t, int slot) {
   constexpr int kTileCh = GATEUP ? TBN / 2 : TBN;  // output channels per tile
-  const int nN = N / kTileCh;
+  const int nN = (N + kTileCh - 1) / kTileCh;       // the last may reach past N
   const int mtiles = rv.tile_off[E];
   const int total = mtiles * nN;
   const int per_xcd = (total + 7) >> 3;
@@ -146,6 +146,7 @@ __device__ __forceinline__ void epilogue(AccT<BM, NW>& acc, const Tile& t,
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int nc = t.n0 + wn * C::CW + i * 32 + 8 * q + 4 * hg;
+        if (nc >= N) continue;  // past the last output channel (N is a multiple of 64)
         float s0[4] = {1.f, 1.f, 1.f, 1.f};
         if (W8) {
 #pragma unroll
@@ -291,7 +292,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dma_kernel(const bf16_bits* __rest
   for (int q = 0; q < D::QW; ++q) {
     const int R = D::WRPI * (q * NW + wave) + lane / D::WCH;
     const int c = dslot<D::WROWB>(R, lane % D::WCH);
-    woff[q] = (uint32_t)((R & (GATEUP ? TBN / 2 - 1 : TBN - 1)) * (K * wsz) + c * 16);
+    // down pass: rows past the last output channel read the last one (their
+    // sums are not stored)
+    const int wr = GATEUP ? (R & (TBN / 2 - 1)) : min(R & (TBN - 1), N - 1 - t.n0);
+    woff[q] = (uint32_t)(wr * (K * wsz) + c * 16);
   }
   auto issue_act = [&](int stage, int buf) {
     char* dst = lds + buf * D::kStageBytes;
@@ -478,7 +482,8 @@ static hipError_t launch_dma(hipStream_t st, const bf16_bits* A, RouteView rv, c
   const hipError_t attr =
       set_lds_limit(reinterpret_cast<const void*>(&dma_kernel<BM, GATEUP, P::NW, P::NS, W8>), lds, lds_set);
   if (attr != hipSuccess) return attr;
-  const dim3 grid(tiled_blocks(BM, rows_cap, E, N / (GATEUP ? TBN / 2 : TBN)), (unsigned)splits);
+  constexpr int kTileCh = GATEUP ? TBN / 2 : TBN;
+  const dim3 grid(tiled_blocks(BM, rows_cap, E, (N + kTileCh - 1) / kTileCh), (unsigned)splits);
   hipLaunchKernelGGL((dma_kernel<BM, GATEUP, P::NW, P::NS, W8>), grid, dim3(P::NW * 64), lds, st, A, rv, w0, w1,
                      scales, T, K, N, E, Ftot, rows_cap, act, out);
   return hipGetLastError();

@@ -62,7 +62,13 @@ def test_workspace_bytes():
     assert gm.grok_moe_workspace_bytes(0, 6144, 32768, 8, 2) > 0
     # invalid / unsupported shapes report 0
     assert gm.grok_moe_workspace_bytes(8, 6144, 32768, 8, 9) == 0          # k > E
-    assert gm.grok_moe_workspace_bytes(8, 6100, 32768, 8, 2) == 0          # d % 128
+    assert gm.grok_moe_workspace_bytes(8, 6100, 32768, 8, 2) == 0          # d % 64
+    # widths that are multiples of 64 (d) and 128 (f) only: every path takes them, with bf16 and 8-bit
+    # weights (a Mixtral-8x7B-like 4096 x 14336, and 6208 x 1408)
+    for T in (8, 200, 2100):
+        for wdt in (gm.BF16, gm.I8):
+            for d, f in ((320, 384), (6208, 1408), (4096, 14336)):
+                assert gm.grok_moe_workspace_bytes(T, d, f, 8, 2, gm.BF16, wdt) >= 2 * T * f * 2, (T, d, f, wdt)
     assert gm.grok_moe_workspace_bytes(8, 6144, 32768, 257, 2) == 0        # E > 256
     assert gm.grok_moe_workspace_bytes(8, 64, 64, 65, 2, gm.F32, gm.F32) == 0   # fp32 router: E <= 64
     # many experts: the router's split-K logits [S][T][E] fp64 are part of the workspace
@@ -114,8 +120,8 @@ def _call(a, ws=0x1000000, ws_bytes=1 << 40):
     (dict(n_shared=-1), gm.EINVAL),
     (dict(router_bias=0x80004), gm.EALIGN),
     (dict(d=200), gm.EUNSUPPORTED),
-    (dict(d=384), gm.EUNSUPPORTED),
-    (dict(f=384), gm.EUNSUPPORTED),
+    (dict(d=352), gm.EUNSUPPORTED),                  # bf16 / 8-bit weights: d % 64
+    (dict(f=320), gm.EUNSUPPORTED),                  # f % 128
     (dict(T=(1 << 20) + 1), gm.EUNSUPPORTED),
     (dict(x=0x10008), gm.EALIGN),
     (dict(w_up=0x40004), gm.EALIGN),

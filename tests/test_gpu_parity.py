@@ -284,3 +284,44 @@ def test_non_finite_tokens_stay_local(E, k, ns):
     assert normwise_err(got[clean], ref["out"]) <= TOL["bf16"]
     # the routing of the bad tokens is valid or dropped (-1), never outside [0, E + ns)
     assert np.all((dbg["idx"][bad] >= -1) & (dbg["idx"][bad] < E + ns))
+
+
+@pytest.mark.parametrize("T,d,f,w_dtype", [
+    (5, 320, 384, "bf16"),       # weight streaming; the down pass's last 128-channel workgroup is half past d
+    (40, 448, 384, "bf16"),
+    (24, 320, 384, "i8"),        # 8-bit weights with d % 128 != 0 take the tiled path even at small T
+    (200, 320, 384, "i8"),
+    (200, 320, 384, "bf16"),     # tiled, 128-row tiles; the down pass's 256-channel tile is ragged
+    (700, 448, 1408, "bf16"),    # tiled, 256-row tiles
+    (2100, 320, 384, "bf16"),    # ping-pong tiles (525 rows per expert)
+    (8, 6208, 1408, "bf16"),     # d = 97 x 64, f = 11 x 128
+    (8, 6208, 1408, "i8"),
+    (2100, 6208, 1408, "bf16"),
+])
+def test_widths_multiple_of_64_and_128(T, d, f, w_dtype):
+    # the boundary takes d % 64 == 0 and f % 128 == 0: every kernel family runs ragged last channel tiles
+    # of the down projection (output channels past d are computed from clamped weight rows and not stored)
+    w = synthetic.make("decode", T=T, d=d, f=f, seed=T + d + f, w_dtype=w_dtype)
+    if w_dtype == "i8":
+        w.scales = synthetic.random_scales(w.E, w.d, w.f, seed=d)
+    got, dbg = run_layer(w, torch)
+    probs, oidx, _ = oracle.route(w.x, w.router_w, w.k)
+    check_routing(dbg["idx"], dbg["gate"], probs)
+    check_permutation(dbg["idx"], dbg, w.E)
+    gates = np.take_along_axis(probs, dbg["idx"].astype(np.int64), 1)
+    toks = None
+    if T * d * f > 2e9:   # sample: both edges of every 256-row tile of every expert, and 24 random tokens
+        offs, perm = dbg["offsets"], dbg["perm"]
+        pick = set(np.random.default_rng(T).choice(T, 24, replace=False).tolist())
+        for e in range(w.E):
+            n = int(offs[e + 1] - offs[e])
+            for m0 in range(0, n, 256):
+                pick.update((int(perm[offs[e] + m0]), int(perm[offs[e] + min(n, m0 + 256) - 1])))
+        toks = sorted(pick)
+    ref = oracle.forward_given_routing(w.x, w.w_gate, w.w_up, w.w_down, dbg["idx"], gates, scales=w.scales,
+                                       tokens=toks)
+    sub = got if toks is None else got[toks]
+    err = normwise_err(sub, ref)
+    tol = TOL["i8" if w_dtype == "i8" else "bf16"]
+    print(f"[widths] T={T} d={d} f={f} {w_dtype}: {len(sub)} tokens, normwise error {err:.3e}", flush=True)
+    assert err <= tol and np.all(np.isfinite(got))
