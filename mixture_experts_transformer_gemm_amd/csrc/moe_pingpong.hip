@@ -326,24 +326,38 @@ __global__ __launch_bounds__(512, 1) void pp_kernel(const bf16_bits* __restrict_
 
   // epilogue: this lane's rows 32 (s + 4 j) + r32 of the tile
   if (GATEUP) {
+    // The 256 x 128 H tile goes through LDS (256-byte rows; 16-byte chunk c
+    // of row R at slot c ^ (R mod 16)), so that every row leaves as whole
+    // 128-byte lines, 16 bytes per lane, instead of 8-byte pieces from four
+    // wavefronts.
     bf16_bits* H = (bf16_bits*)out;
+    __syncthreads();  // every wavefront is past its last fragment read
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int m = 32 * (s + 4 * j) + r32;
-      if (m < t.M) {
-        bf16_bits* hrow = H + (int64_t)(t.m0 + m) * N + t.n0 + 64 * g;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float h[4];
+        for (int q = 0; q < 4; ++q) {
+          float h[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) h[v] = glu_act(act, acc[i][j][4 * q + v]) * acc[i + 2][j][4 * q + v];
-            uint2 o;
-            o.x = pack_bf16x2(h[0], h[1]);
-            o.y = pack_bf16x2(h[2], h[3]);
-            *reinterpret_cast<uint2*>(hrow + 32 * i + 8 * q + 4 * hg) = o;
-          }
+          for (int v = 0; v < 4; ++v) h[v] = glu_act(act, acc[i][j][4 * q + v]) * acc[i + 2][j][4 * q + v];
+          uint2 o;
+          o.x = pack_bf16x2(h[0], h[1]);
+          o.y = pack_bf16x2(h[2], h[3]);
+          const int c = 8 * g + 4 * i + q;  // 16-byte chunk of the 128 channels
+          *reinterpret_cast<uint2*>(lds + m * 256 + ((c ^ (m & 15)) * 16) + 8 * hg) = o;
+        }
+    }
+    __syncthreads();
+    // wavefront w stores rows 32 w .. 32 w + 31, four rows per instruction
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int R = 32 * wave + 4 * it + (lane >> 4);
+      const int c = lane & 15;
+      if (R < t.M) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + R * 256 + ((c ^ (R & 15)) * 16));
+        *reinterpret_cast<u32x4*>(H + (int64_t)(t.m0 + R) * N + t.n0 + 8 * c) = v;
       }
     }
   } else {
