@@ -361,21 +361,35 @@ __global__ __launch_bounds__(512, 1) void pp_kernel(const bf16_bits* __restrict_
       }
     }
   } else {
+    // The 256 x 256 fp32 tile goes through LDS in two passes of 128 rows
+    // (1 KB rows; 16-byte chunk c of row R at slot c ^ (R mod 16)): pass p
+    // holds every wavefront's row tile j = p, and each row then leaves as one
+    // 1 KB store (16 bytes per lane) instead of 32-byte pieces of 32 rows
+    // per instruction (those took a fifth of the down pass).
     float* Y = (float*)out + (int64_t)sp * rows_cap * N;
+    const int nleft = N - t.n0;  // output channels of the tile inside N (a multiple of 64)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int m = 32 * (s + 4 * j) + r32;
-      if (m < t.M) {
-        float* yrow = Y + (int64_t)(t.m0 + m) * N + t.n0 + 128 * g;
-        const int nleft = N - t.n0 - 128 * g;  // channels of this wavefront inside N (a multiple of 64)
+      __syncthreads();  // the LDS is free (loop done, or the previous pass stored)
+      const int m = 32 * s + r32;  // row within this pass
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (32 * i < nleft) {
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              *reinterpret_cast<float4*>(yrow + 32 * i + 8 * q + 4 * hg) =
-                  make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-          }
+        for (int q = 0; q < 4; ++q) {
+          const int c = 32 * g + 8 * i + 2 * q + hg;  // 16-byte chunk: channels 4 c .. 4 c + 3
+          *reinterpret_cast<float4*>(lds + m * 1024 + ((c ^ (m & 15)) * 16)) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
+      __syncthreads();
+      // wavefront w stores rows 16 w .. 16 w + 15 of the pass, one row per instruction
+#pragma unroll 4
+      for (int it = 0; it < 16; ++it) {
+        const int R = 16 * wave + it;
+        const int row = 128 * j + R;
+        if (row < t.M && 4 * lane < nleft) {
+          const float4 v = *reinterpret_cast<const float4*>(lds + R * 1024 + ((lane ^ (R & 15)) * 16));
+          *reinterpret_cast<float4*>(Y + (int64_t)(t.m0 + row) * N + t.n0 + 4 * lane) = v;
+        }
       }
     }
   }
