@@ -14,11 +14,14 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// 4 signed bytes -> 4 bf16 (exact: |q| <= 127 needs 7 significant bits)
+// 2 signed bytes (bits sh.. of w) -> 2 bf16 (exact: |q| <= 128 needs at
+// most 8 significant bits): each byte converts to fp32, and one byte permute
+// takes the upper halves of both (v_perm_b32 selectors 0-3 pick bytes of its
+// second operand, 4-7 of its first)
 __device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, int sh) {
   const float a = (float)(int)(int8_t)(w >> sh);
   const float b = (float)(int)(int8_t)(w >> (sh + 8));
-  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
 // 16 int8 (one 16-byte load) -> two fragments of 8 bf16
 __device__ __forceinline__ void i8x16_to_frags(u32x4 q, u32x4& lo, u32x4& hi) {
