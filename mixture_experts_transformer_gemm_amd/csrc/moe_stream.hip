@@ -47,6 +47,7 @@
 #include "moe_device.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace gmoe {
 
@@ -98,6 +99,16 @@ struct BsCfg {
 // slot of 16-byte chunk c of a 256-byte activation row r (16 chunks; the 16
 // rows read at one chunk land in 16 distinct bank groups)
 __device__ __forceinline__ int aslot256(int r, int c) { return c ^ (r & 15); }
+
+// f(integral_constant<int, u>) for u = 0 .. N-1, unrolled
+template <class F, int... U>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, U...>) {
+  (f(std::integral_constant<int, U>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
 
 // s_waitcnt vmcnt(p * Q) for a run-time p in [0, 6]
 template <int Q>
@@ -279,13 +290,20 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
       }
     }
   };
-  // MV: tiles that get MFMAs (the chunk's rows rounded up to MT/4 (chunks
-  // of 64 rows or more), MT/2, 3MT/4 (128-row chunks only) or MT tiles; rows
-  // past the segment's end repeat its last row)
+  // MV: tiles that get MFMAs. 8-bit weights: exactly the 16-row tiles that
+  // hold rows (the stage is bound by its MFMA and LDS work, both linear in
+  // MV: at 256 Grok-1 tokens 5 of 8 experts hold 65-71 rows, 80 rows of work
+  // instead of 96). bf16: the chunk's rows rounded up to MT/4 (chunks of 64
+  // rows or more), MT/2 or MT tiles. Rows past the segment's end repeat its
+  // last row.
   constexpr int kHalf = MT > 1 ? MT / 2 : 1;
   constexpr int kQuarter = MT >= 4 ? MT / 4 : kHalf;
   auto run_naw = [&](auto naw_tag) __attribute__((always_inline)) {
-    if (kQuarter < kHalf && mv <= kQuarter)
+    if constexpr (W8) {
+      static_for<MT>([&](auto u_tag) __attribute__((always_inline)) {
+        if (mv == decltype(u_tag)::value + 1) run(naw_tag, std::integral_constant<int, decltype(u_tag)::value + 1>{});
+      });
+    } else if (kQuarter < kHalf && mv <= kQuarter)
       run(naw_tag, std::integral_constant<int, kQuarter>{});
     else if (mv <= kHalf)
       run(naw_tag, std::integral_constant<int, kHalf>{});

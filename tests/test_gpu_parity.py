@@ -239,12 +239,16 @@ def test_permutation_many_blocks(E, k, cf):
 @pytest.mark.parametrize("w_dtype,T,sizes", [("bf16", 1100, [0, 1, 319, 320, 321, 640, 599, 0]),
                                               ("bf16", 1100, [0, 255, 256, 257, 512, 513, 1, 406]),
                                               ("bf16", 2100, [0, 255, 256, 257, 1024, 1025, 1, 1382]),
-                                              ("i8", 1100, [0, 1, 319, 320, 321, 640, 599, 0])])
+                                              ("i8", 1100, [0, 1, 319, 320, 321, 640, 599, 0]),
+                                              ("i8", 228, [1, 17, 33, 49, 65, 81, 97, 113]),
+                                              ("i8", 64, [1, 17, 33, 49, 28, 0, 0, 0])])
 def test_tile_boundaries_and_empty_experts(w_dtype, T, sizes):
     # 1,100 tokens at top-2 average 275 rows per expert, so bf16 weights run 320-row tiles (8-bit: 128-row);
     # 2,100 tokens average 525, which runs the 256-row ping-pong tiles. Segments of 0, 1, 255 .. 257,
     # 319 .. 321, 512, 513, 640, 1024 and 1025 rows put tile edges on both sides of every boundary, and
-    # empty first and last experts must be skipped by the tile table
+    # empty first and last experts must be skipped by the tile table. With 8-bit weights and 65 .. 256
+    # (up to 64) tokens the streaming kernel runs 128-row (64-row) chunks, and segments of 1, 17, .., 113
+    # rows take every count of 16-row MFMA tiles it computes (1 .. 8, or 1 .. 4)
     E, k = 8, 2
     assert sum(sizes) == T * k
     labels = np.repeat(np.arange(E, dtype=np.int32), sizes)            # sorted by expert, 2T long
