@@ -44,11 +44,36 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
-// Exact-erf GELU: z * Phi(z) = z (1 + erf(z / sqrt 2)) / 2, with the device library's erff.
-__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+// Exact-erf GELU: z * Phi(z), Phi(z) = erfc(-z / sqrt 2) / 2. Phi(-|z|) = erfc(u) / 2 with
+// u = |z| / sqrt 2 comes from the Chebyshev fit of Numerical Recipes (Press et al., 2nd ed., section
+// 6.2, erfcc): erfc(u) = t exp(P(t) - u^2), t = 2 / (2 + u), P of degree 9, fractional error below
+// 1.2e-7 for every u >= 0; Phi(|z|) = 1 - Phi(-|z|). Branch-free: one v_rcp_f32, ten FMAs and one
+// v_exp_f32 (about 1 ulp each), where the device library's erff costs about 70 instructions with
+// divergent range branches. Evaluated in fp32 against the fp64 GELU: relative error below 1e-6 for
+// |z| <= 4, below 2e-5 everywhere (the far negative tail, where the exponent is large), absolute
+// error below 4e-7. In the gate/up epilogue of a 256 x 256 prefill tile this was 15% of the tile time.
+__device__ __forceinline__ float gelu_erf(float z) {
+  const float u = fabsf(z) * 0.70710678118654752f;
+  const float t = 2.0f * __builtin_amdgcn_rcpf(2.0f + u);
+  float p = 0.17087277f;
+  p = fmaf(p, t, -0.82215223f);
+  p = fmaf(p, t, 1.48851587f);
+  p = fmaf(p, t, -1.13520398f);
+  p = fmaf(p, t, 0.27886807f);
+  p = fmaf(p, t, -0.18628806f);
+  p = fmaf(p, t, 0.09678418f);
+  p = fmaf(p, t, 0.37409196f);
+  p = fmaf(p, t, 1.00002368f);
+  p = fmaf(p, t, -1.26551223f);
+  const float q = 0.5f * t * __builtin_amdgcn_exp2f((p - u * u) * 1.44269504088896341f);  // Phi(-|z|)
+  return z * (z >= 0.0f ? 1.0f - q : q);
+}
 
-// SiLU: z * sigmoid(z) = z / (1 + e^-z), with the device library's expf (z -> -inf gives -0).
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// SiLU: z * sigmoid(z) = z / (1 + e^-z), with v_exp_f32 and v_rcp_f32 (about 1 ulp each; z -> -inf
+// gives e^-z = inf and -0).
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.44269504088896341f));
+}
 
 // Activation of the gate branch: ACT_GELU (Grok-1's GeGLU experts) or ACT_SILU
 // (SwiGLU experts). The flag is uniform over a launch.

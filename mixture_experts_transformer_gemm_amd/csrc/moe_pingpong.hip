@@ -332,23 +332,33 @@ __global__ __launch_bounds__(512, 1) void pp_kernel(const bf16_bits* __restrict_
     // wavefronts.
     bf16_bits* H = (bf16_bits*)out;
     __syncthreads();  // every wavefront is past its last fragment read
+    // the activation is uniform over the launch: one branch around the whole tile
+    auto stage_h = [&](auto silu_tag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int m = 32 * (s + 4 * j) + r32;
+      for (int j = 0; j < 2; ++j) {
+        const int m = 32 * (s + 4 * j) + r32;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float h[4];
+          for (int q = 0; q < 4; ++q) {
+            float h[4];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) h[v] = glu_act(act, acc[i][j][4 * q + v]) * acc[i + 2][j][4 * q + v];
-          uint2 o;
-          o.x = pack_bf16x2(h[0], h[1]);
-          o.y = pack_bf16x2(h[2], h[3]);
-          const int c = 8 * g + 4 * i + q;  // 16-byte chunk of the 128 channels
-          *reinterpret_cast<uint2*>(lds + m * 256 + ((c ^ (m & 15)) * 16) + 8 * hg) = o;
-        }
-    }
+            for (int v = 0; v < 4; ++v) {
+              const float z = acc[i][j][4 * q + v];
+              h[v] = (decltype(silu_tag)::value ? silu(z) : gelu_erf(z)) * acc[i + 2][j][4 * q + v];
+            }
+            uint2 o;
+            o.x = pack_bf16x2(h[0], h[1]);
+            o.y = pack_bf16x2(h[2], h[3]);
+            const int c = 8 * g + 4 * i + q;  // 16-byte chunk of the 128 channels
+            *reinterpret_cast<uint2*>(lds + m * 256 + ((c ^ (m & 15)) * 16) + 8 * hg) = o;
+          }
+      }
+    };
+    if (act == ACT_SILU)
+      stage_h(std::true_type{});
+    else
+      stage_h(std::false_type{});
     __syncthreads();
     // wavefront w stores rows 32 w .. 32 w + 31, four rows per instruction
 #pragma unroll
