@@ -302,6 +302,18 @@ def measure(torch, gm, HipEvents, w, tensors, variant, out, ws, stream, counts, 
                  "algorithmic_per_launch": gu_bytes if hbm_bound else gu_flops,
                  "avg_launch_ms": round(gate_up_ms, 5), "traffic_source": traffic_note})
     layer_s = ms_per_step / 1e3
+    # Per-expert split of the two grouped GEMMs' time (a model, stated as such): every row tile of an
+    # expert reads that expert's weights for its output channels and runs tile_rows rows of matrix-core
+    # work whatever its fill, so the GEMM time divides by tile count, not by rows.
+    tile_rows = gm.grok_moe_tile_rows(x, rw, wg, wu, wd, k=w.k, **variant)
+    split = None
+    if tile_rows and len(counts) <= 16:
+        tiles = [-(-int(c) // tile_rows) for c in counts]
+        gemm_ms = stage_ms["gate_up"] + stage_ms["down"]
+        split = {"model": "gate_up+down time x (expert's row tiles / all row tiles)", "tile_rows": tile_rows,
+                 "experts": [{"expert": e, "rows": int(c), "row_tiles": n, "empty_rows": n * tile_rows - int(c),
+                              "gemm_ms": round(gemm_ms * n / max(sum(tiles), 1), 4)}
+                             for e, (c, n) in enumerate(zip(counts, tiles))]}
     return {
         "metric": METRIC,
         "value": round(tokens_per_s, 2),
@@ -327,7 +339,7 @@ def measure(torch, gm, HipEvents, w, tensors, variant, out, ws, stream, counts, 
                   "mfma_frac": round(layer_flops / layer_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                   "hbm_frac": round(layer_bytes / layer_s / 1e9 / HBM_PEAK_GBS, 4),
                   "stage_ms": {k2: round(v, 5) for k2, v in stage_ms.items()},
-                  "device_step_ms": step_dist, "breakdown_steps": nb},
+                  "device_step_ms": step_dist, "breakdown_steps": nb, "expert_split": split},
     }
 
 

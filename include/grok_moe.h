@@ -179,6 +179,16 @@ size_t grok_moe_workspace_bytes(int64_t T, int64_t d, int64_t f, int32_t E, int3
  * type and n_shared fields are read. 0 for an invalid or unsupported shape. */
 size_t grok_moe_workspace_bytes_ex(const grok_moe_args* a);
 
+/* Rows per tile of the grouped GEMMs that grok_moe_forward_ex runs for the
+ * sizes, dtypes and variant knobs of `a` (its pointers are not read): each
+ * expert's rows run as ceil(rows / tile_rows) tiles, and every tile reads that
+ * expert's weights for the tile's output channels, so an expert's GEMM time
+ * follows its tile count rather than its rows. 16, 32, 64 or 128 on the
+ * streaming (small-batch) path, 64, 128, 256 or 320 on the tiled path. Returns
+ * 0 for a shape grok_moe_forward_ex rejects, and for fp32 activations, whose
+ * kernels have no row tiles. Host only; enqueues nothing. */
+int32_t grok_moe_tile_rows(const grok_moe_args* a);
+
 /* The layer with caller-owned workspace (ws: device memory, 256-byte aligned,
  * at least grok_moe_workspace_bytes(); its contents on entry do not matter and
  * are clobbered). dbg may be NULL. Allocates nothing. */

@@ -31,8 +31,9 @@ ACT_GELU, ACT_SILU = 0, 1
 OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
 STAGES = ("router", "permute", "gate_up", "down", "combine")
 
-EXPORTED = ("grok_moe_workspace_bytes", "grok_moe_workspace_bytes_ex", "grok_moe_forward_ex", "grok_moe_forward",
-            "grok_moe_forward_w8", "grok_moe_forward_f32", "grok_moe_forward_static", "grok_moe_status_string")
+EXPORTED = ("grok_moe_workspace_bytes", "grok_moe_workspace_bytes_ex", "grok_moe_tile_rows", "grok_moe_forward_ex",
+            "grok_moe_forward", "grok_moe_forward_w8", "grok_moe_forward_f32", "grok_moe_forward_static",
+            "grok_moe_status_string")
 STATIC_WORKSPACE_BYTES = 64 << 20   # GROK_MOE_STATIC_WORKSPACE_BYTES
 
 
@@ -75,6 +76,8 @@ def lib():
         h.grok_moe_workspace_bytes.restype = ctypes.c_size_t
         h.grok_moe_workspace_bytes_ex.argtypes = [ctypes.POINTER(Args)]
         h.grok_moe_workspace_bytes_ex.restype = ctypes.c_size_t
+        h.grok_moe_tile_rows.argtypes = [ctypes.POINTER(Args)]
+        h.grok_moe_tile_rows.restype = ctypes.c_int32
         h.grok_moe_forward_ex.argtypes = [ctypes.POINTER(Args), vp, ctypes.c_size_t, ctypes.POINTER(Debug), vp]
         h.grok_moe_forward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
         h.grok_moe_forward_w8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
@@ -103,6 +106,13 @@ def grok_moe_workspace_bytes_ex(x, router_w, w_gate, w_up, w_down, k: int = 2, *
     the 8-bit scales may be left out, and x stands in for out)."""
     a = make_args(x, router_w, w_gate, w_up, w_down, x, k, sizing=True, **variant)
     return int(lib().grok_moe_workspace_bytes_ex(ctypes.byref(a)))
+
+
+def grok_moe_tile_rows(x, router_w, w_gate, w_up, w_down, k: int = 2, **variant) -> int:
+    """Rows per grouped-GEMM tile that grok_moe_forward_ex runs for these tensors' sizes and dtypes and
+    variant knobs (0 for fp32 activations or a rejected shape)."""
+    a = make_args(x, router_w, w_gate, w_up, w_down, x, k, sizing=True, **variant)
+    return int(lib().grok_moe_tile_rows(ctypes.byref(a)))
 
 
 # ---------------------------------------------------------------- torch marshalling

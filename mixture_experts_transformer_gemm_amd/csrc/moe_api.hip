@@ -244,6 +244,18 @@ size_t grok_moe_workspace_bytes_ex(const grok_moe_args* a) {
   return make_plan(a->T, a->d, a->f, a->E, a->k, a->n_shared, a->act_dtype, a->w_dtype).total;
 }
 
+int32_t grok_moe_tile_rows(const grok_moe_args* a) {
+  if (!a || check_shape(a->T, a->d, a->f, a->E, a->k, a->n_shared, a->act_dtype, a->w_dtype) != GROK_MOE_OK) return 0;
+  const Plan p = make_plan(a->T, a->d, a->f, a->E, a->k, a->n_shared, a->act_dtype, a->w_dtype);
+  if (p.path == PATH_TILED) return p.bm;
+  if (p.path == PATH_STREAM) {
+    // the streaming kernels' chunk: 16, 32, 64 rows, or 128 with 8-bit weights
+    const int64_t r = p.mt_max;
+    return r <= 16 ? 16 : (r <= 32 ? 32 : ((r <= 64 || a->w_dtype != GROK_MOE_I8) ? 64 : 128));
+  }
+  return 0;
+}
+
 int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const grok_moe_debug* dbg,
                         void* stream) {
   int rc = validate(a);

@@ -162,6 +162,22 @@ def test_workspace_bytes_ex_counts_shared_experts():
     assert gm.lib().grok_moe_workspace_bytes_ex(ctypes.byref(a)) == 0
 
 
+@pytest.mark.parametrize("kw,rows", [
+    (dict(T=8, d=6144, f=32768), 16),                                   # Grok-1 decode: streaming, 16-row chunks
+    (dict(T=64, d=6144, f=32768), 64),
+    (dict(T=256, d=6144, f=32768, w_dtype=gm.I8), 128),                # 8-bit streaming, 128-row chunks
+    (dict(T=8192, d=6144, f=32768), 256),                               # prefill: ping-pong 256-row tiles
+    (dict(T=8192, d=6144, f=32768, w_dtype=gm.I8), 256),
+    (dict(T=1100, d=256, f=512), 320),                                  # 275 rows per expert
+    (dict(T=8192, d=7168, f=2048, E=256, k=8, n_shared=1), 320),        # 287 rows per expert
+    (dict(T=300, d=256, f=512, w_dtype=gm.I8), 128),
+    (dict(T=64, d=256, f=512, act_dtype=gm.F32, w_dtype=gm.F32), 0),   # fp32: no row tiles
+    (dict(T=8, k=9), 0),                                                # rejected shape
+])
+def test_tile_rows(kw, rows):
+    assert gm.lib().grok_moe_tile_rows(ctypes.byref(_args(**kw))) == rows
+
+
 def test_ctypes_structs_match_the_header(tmp_path):
     # offsets and sizes of grok_moe_args / grok_moe_debug as the C compiler lays them out
     fields = {"grok_moe_args": gm.Args, "grok_moe_debug": gm.Debug}

@@ -9,11 +9,13 @@ that workload) and random tokens. Both the
 per-token normwise error (the tolerance) and the elementwise error with a floor
 of a thousandth of the token's largest value are computed and printed.
 """
+import ctypes
 import gc
 
 import numpy as np
 import pytest
 
+import mixture_experts_transformer_gemm_amd as gm
 import oracle
 import synthetic
 from gpu_util import TOL, check_permutation, check_routing, elementwise_err, normwise_err, run_layer
@@ -48,14 +50,13 @@ def _sample_tokens(dbg, E, n_random, seed, bm=None):
 
 
 def _tile_height(w):
-    """Row-tile height the library's plan picks for this shape (average rows per expert r): 64 up to 32
-    rows, 128 up to 96, 256 beyond, 320 past 256 rows with bf16 weights; 8-bit weights use 128 up to 384."""
-    r = w.T * w.k // w.E
-    bm = 64 if r <= 32 else (128 if r <= 96 else 256)
-    if w.w_dtype == "bf16" and r > 256:
-        bm = 320
-    if w.w_dtype == "i8" and r <= 384:
-        bm = 128
+    """Row-tile height the library runs for this workload's shape (grok_moe_tile_rows)."""
+    a = gm.Args()
+    a.T, a.d, a.f, a.E, a.k, a.n_shared = w.T, w.d, w.f, w.E, w.k, w.n_shared
+    a.act_dtype = gm.F32 if w.act_dtype == "f32" else gm.BF16
+    a.w_dtype = {"bf16": gm.BF16, "i8": gm.I8, "f32": gm.F32}[w.w_dtype]
+    bm = gm.lib().grok_moe_tile_rows(ctypes.byref(a))
+    assert bm > 0
     return bm
 
 
