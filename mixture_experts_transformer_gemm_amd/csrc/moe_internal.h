@@ -49,9 +49,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // 6.2, erfcc): erfc(u) = t exp(P(t) - u^2), t = 2 / (2 + u), P of degree 9, fractional error below
 // 1.2e-7 for every u >= 0; Phi(|z|) = 1 - Phi(-|z|). Branch-free: one v_rcp_f32, ten FMAs and one
 // v_exp_f32 (about 1 ulp each), where the device library's erff costs about 70 instructions with
-// divergent range branches. Evaluated in fp32 against the fp64 GELU: relative error below 1e-6 for
-// |z| <= 4, below 2e-5 everywhere (the far negative tail, where the exponent is large), absolute
-// error below 4e-7. In the gate/up epilogue of a 256 x 256 prefill tile this was 15% of the tile time.
+// divergent range branches. Evaluated in fp32 against the fp64 GELU: relative error below 3e-6 for
+// |z| <= 4, below 2e-5 everywhere (the far negative tail, where the rounding of the exponent grows),
+// absolute error below 4e-7.
 __device__ __forceinline__ float gelu_erf(float z) {
   const float u = fabsf(z) * 0.70710678118654752f;
   const float t = 2.0f * __builtin_amdgcn_rcpf(2.0f + u);
