@@ -55,8 +55,9 @@
 // loads alone (almost no MFMAs) take about as long as the MFMAs alone, and the
 // two overlap only in part. The waits for loads are a few percent of the
 // loop: the limit is the rate at which the memory system delivers the 64 KB
-// of a slice (L2 hit rate about 55%), and with random bf16 operands the chip
-// also holds a lower clock under full MFMA load.
+// of a slice (L2 hit rate 0.78 in the gate/up pass, 0.75 in the down pass),
+// and with random bf16 operands the chip holds about 1.6 GHz under this load
+// (MFMA busy 0.69 / 0.74 of the CU-busy cycles).
 #include "moe_device.h"
 
 #include <type_traits>

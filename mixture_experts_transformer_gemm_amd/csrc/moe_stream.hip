@@ -140,13 +140,18 @@ __global__ __launch_bounds__(kBW * 64) void stream_kernel(const bf16_bits* __res
   // workgroups per expert; the last one may reach past N (the down pass with
   // d % 128 != 0): its wavefronts past N read clamped weight rows, store nothing
   const int nblk = (N + kBW * kChW - 1) / (kBW * kChW);
-  // Down pass with E % 8 == 0: workgroup x runs on XCD x mod 8, and the
-  // order below keeps all of expert e's workgroups on XCD e mod 8, so its H
-  // rows are fetched into one L2 instead of eight (measured 2-3% faster on
-  // the down pass; the gate/up pass, whose x rows are few, measured slower
-  // with it).
+  // Down pass with E % 8 == 0 (E <= 64) and every expert holding rows:
+  // workgroup x runs on XCD x mod 8, and the order below keeps all of expert
+  // e's workgroups on XCD e mod 8, so its H rows are fetched into one L2
+  // instead of eight (measured 2-3% faster on the down pass; the gate/up
+  // pass, whose x rows are few, measured slower with it). With an expert
+  // empty its XCD would idle (one token: 2 of 8 experts, the down pass 2.7x
+  // slower), so then every expert's workgroups stay spread over all XCDs.
+  bool by_xcd = !GATEUP && (E & 7) == 0 && E <= 64;
+  if (by_xcd)
+    for (int i = 0; i < E; ++i) by_xcd = by_xcd && rv.counts[i] > 0;
   int e, nb;
-  if (!GATEUP && (E & 7) == 0) {
+  if (by_xcd) {
     const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
     e = xcd + 8 * (i / nblk);
     nb = i - (i / nblk) * nblk;
