@@ -17,8 +17,9 @@
 // epilogue).
 //
 // Workgroup = 8 wavefronts, each streaming its own 16 weight rows (32 for
-// 8-bit weights in chunks of more than 32 rows, where the activation
-// fragment reads bound the stage: each fragment then feeds two MFMAs). The
+// 8-bit weights: each activation fragment read from LDS then feeds two
+// MFMAs, and 8-bit rows are half as long, so a workgroup keeps a long
+// stream). The
 // segment's activation rows (token rows of x through the permutation, or H
 // rows) of each stage are loaded once per workgroup, spread over the
 // wavefronts for as many load instructions as the rows need, and shared by
