@@ -86,7 +86,10 @@ struct BsCfg {
   static constexpr int NI = XR / ARPI;                   // activation load instructions per stage (max)
   static constexpr int kQA = (NI + kBW - 1) / kBW;       // of which one wavefront issues at most
   static constexpr int kActOff = kBWRows * kRowB;        // activation rows follow the weight rows
-  static constexpr int kLdsBytes = 147456;                // ring space: 144 KB
+  // ring space: all 160 KB (one workgroup per CU either way; with 8-bit
+  // weights and 65-80 rows a stage is 52 KB, so 3 stages fit instead of 2:
+  // 2% off both 8-bit passes at 256 tokens, neutral elsewhere)
+  static constexpr int kLdsBytes = 163840;
   // Ring of a workgroup whose chunk needs MV 16-row tiles: its stages hold
   // only those activation rows, so fewer rows leave room for more stages
   // (as many as fit in the ring space, at most 8).
