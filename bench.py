@@ -306,14 +306,7 @@ def measure(torch, gm, HipEvents, w, tensors, variant, out, ws, stream, counts, 
     # expert reads that expert's weights for its output channels and runs tile_rows rows of matrix-core
     # work whatever its fill, so the GEMM time divides by tile count, not by rows.
     tile_rows = gm.grok_moe_tile_rows(x, rw, wg, wu, wd, k=w.k, **variant)
-    split = None
-    if tile_rows and len(counts) <= 16:
-        tiles = [-(-int(c) // tile_rows) for c in counts]
-        gemm_ms = stage_ms["gate_up"] + stage_ms["down"]
-        split = {"model": "gate_up+down time x (expert's row tiles / all row tiles)", "tile_rows": tile_rows,
-                 "experts": [{"expert": e, "rows": int(c), "row_tiles": n, "empty_rows": n * tile_rows - int(c),
-                              "gemm_ms": round(gemm_ms * n / max(sum(tiles), 1), 4)}
-                             for e, (c, n) in enumerate(zip(counts, tiles))]}
+    split = expert_split(counts, tile_rows, stage_ms["gate_up"] + stage_ms["down"]) if len(counts) <= 16 else None
     return {
         "metric": METRIC,
         "value": round(tokens_per_s, 2),
@@ -341,6 +334,19 @@ def measure(torch, gm, HipEvents, w, tensors, variant, out, ws, stream, counts, 
                   "stage_ms": {k2: round(v, 5) for k2, v in stage_ms.items()},
                   "device_step_ms": step_dist, "breakdown_steps": nb, "expert_split": split},
     }
+
+
+def expert_split(counts, tile_rows, gemm_ms):
+    """Per-expert share of the two grouped GEMMs' time, modelled by row tiles: an expert with c rows runs
+    ceil(c / tile_rows) tiles, each reading the expert's weights for its channels and doing tile_rows rows
+    of matrix-core work whatever its fill. None when the shape has no row tiles (tile_rows 0)."""
+    if not tile_rows:
+        return None
+    tiles = [-(-int(c) // tile_rows) for c in counts]
+    total = max(sum(tiles), 1)
+    return {"model": "gate_up+down time x (expert's row tiles / all row tiles)", "tile_rows": int(tile_rows),
+            "experts": [{"expert": e, "rows": int(c), "row_tiles": n, "empty_rows": n * tile_rows - int(c),
+                         "gemm_ms": round(gemm_ms * n / total, 4)} for e, (c, n) in enumerate(zip(counts, tiles))]}
 
 
 def _cpu_model():

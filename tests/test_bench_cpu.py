@@ -65,3 +65,19 @@ def test_oracle_sample_covers_every_expert():
         have = np.isin(s, perm[offsets[e]:offsets[e + 1]]).sum()
         assert have >= min(8, counts[e]), (e, have)
     assert np.array_equal(s, bench.oracle_sample(perm, offsets, T, n=256, per_expert=8, seed=0))
+
+
+def test_expert_split_divides_by_row_tiles():
+    # the skewed 2048-token routing at 256-row tiles: 19 row tiles, the cold experts one each
+    counts = [1958, 1247, 146, 152, 136, 163, 143, 151]
+    s = bench.expert_split(counts, 256, 4.75)
+    assert s["tile_rows"] == 256
+    tiles = [e["row_tiles"] for e in s["experts"]]
+    assert tiles == [8, 5, 1, 1, 1, 1, 1, 1]
+    assert [e["empty_rows"] for e in s["experts"]] == [90, 33, 110, 104, 120, 93, 113, 105]
+    assert sum(e["gemm_ms"] for e in s["experts"]) == pytest.approx(4.75, abs=1e-3)
+    assert s["experts"][0]["gemm_ms"] == pytest.approx(4.75 * 8 / 19, abs=1e-4)
+    # an expert without rows runs no tile; no row tiles at all (fp32 path) gives no split
+    z = bench.expert_split([0, 300], 128, 1.0)
+    assert [e["row_tiles"] for e in z["experts"]] == [0, 3] and z["experts"][0]["gemm_ms"] == 0.0
+    assert bench.expert_split([5, 5], 0, 1.0) is None
