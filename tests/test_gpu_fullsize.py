@@ -115,6 +115,12 @@ def test_skew_full():
     assert share[0] > 0.4 and share[1] > 0.22
 
 
+def test_int8_prefill_full():
+    # 8-bit weights at the prefill size: the 8-bit ping-pong kernel (256-row tiles, pairs of slices)
+    dbg, counts = _run_and_check("int8", n_random=6, T=8192)
+    assert counts.sum() == 2 * 8192
+
+
 def test_prefill_full():
     dbg, counts = _run_and_check("prefill", n_random=6)
     pairs = {tuple(sorted(p)) for p in dbg["idx"].tolist()}
