@@ -52,7 +52,7 @@ def test_bf16_layer_other_shapes(T, d, f):
     _full_check(w)
 
 
-@pytest.mark.parametrize("T", [3, 24, 40, 128, 200, 513, 1600])
+@pytest.mark.parametrize("T", [3, 24, 40, 128, 200, 513, 1600, 2049, 4100])
 def test_int8_layer_small_random_scales(T):
     # distinct per-channel scales pin which output channel each scale belongs to
     w = synthetic.make("int8", T=T, d=256, f=512, seed=T)
@@ -240,11 +240,12 @@ def test_permutation_many_blocks(E, k, cf):
                                               ("bf16", 1100, [0, 255, 256, 257, 512, 513, 1, 406]),
                                               ("bf16", 2100, [0, 255, 256, 257, 1024, 1025, 1, 1382]),
                                               ("i8", 1100, [0, 1, 319, 320, 321, 640, 599, 0]),
+                                              ("i8", 2100, [0, 255, 256, 257, 1024, 1025, 1, 1382]),
                                               ("i8", 228, [1, 17, 33, 49, 65, 81, 97, 113]),
                                               ("i8", 64, [1, 17, 33, 49, 28, 0, 0, 0])])
 def test_tile_boundaries_and_empty_experts(w_dtype, T, sizes):
     # 1,100 tokens at top-2 average 275 rows per expert, so bf16 weights run 320-row tiles (8-bit: 128-row);
-    # 2,100 tokens average 525, which runs the 256-row ping-pong tiles. Segments of 0, 1, 255 .. 257,
+    # 2,100 tokens average 525, which runs the 256-row ping-pong tiles (8-bit: tiled, 256-row). Segments of 0, 1, 255 .. 257,
     # 319 .. 321, 512, 513, 640, 1024 and 1025 rows put tile edges on both sides of every boundary, and
     # empty first and last experts must be skipped by the tile table. With 8-bit weights and 65 .. 256
     # (up to 64) tokens the streaming kernel runs 128-row (64-row) chunks, and segments of 1, 17, .., 113
@@ -301,6 +302,7 @@ def test_non_finite_tokens_stay_local(E, k, ns):
     (8, 6208, 1408, "bf16"),     # d = 97 x 64, f = 11 x 128
     (8, 6208, 1408, "i8"),
     (2100, 6208, 1408, "bf16"),
+    (2100, 384, 1408, "i8"),     # 8-bit at 525 rows per expert: tiled 256-row tiles, the down pass's last tile half past d
 ])
 def test_widths_multiple_of_64_and_128(T, d, f, w_dtype):
     # the boundary takes d % 64 == 0 and f % 128 == 0: every kernel family runs ragged last channel tiles
