@@ -45,10 +45,10 @@
 // (v mod 4)][l mod 32] (channel, row).
 //
 // Tile order: the tiles that exist are numbered expert by expert; within an
-// expert, groups of 4 row tiles are walked channel tile by channel tile with
+// expert, groups of 8 row tiles are walked channel tile by channel tile with
 // the row tiles fastest; the numbering is split into 8 contiguous ranges, one
 // per XCD (workgroup i runs on XCD i mod 8), so the 32 workgroups resident on
-// an XCD share 4 row tiles of activations and 8 weight tiles through its L2.
+// an XCD share 8 row tiles of activations and 4 weight tiles through its L2.
 //
 // What bounds it (Grok-1 prefill, measured): with no global loads in the loop
 // the gate/up pass runs at 64% of the bf16 peak and the down pass at 75%; the
@@ -72,11 +72,12 @@ constexpr int kPK = 64;           // reduction values per slice
 constexpr int kPRow = kPK * 2;    // LDS bytes per row and slice: one 128-byte line
 constexpr int kPSliceA = kPM * kPRow;  // activation half of a slice: 32 KB
 constexpr int kPSliceW = kPN * kPRow;  // weight half: 32 KB
-// Row tiles per tile group: 32 workgroups resident on one XCD then hold 4
-// row tiles x 8 channel tiles of one expert (measured at the Grok-1 prefill:
-// layer 18.6 ms against 19.3 ms walking all of an expert's row tiles per
-// channel tile, 19.1 with groups of 2 or 3, 18.8 with 5 or 8)
-constexpr int kPGroup = 4;
+// Row tiles per tile group: 32 workgroups resident on one XCD then hold 8
+// row tiles x 4 channel tiles of one expert (measured at the Grok-1 prefill,
+// gate/up launch: 11.08-11.18 ms with groups of 8, 11.38 with 4, 11.54 with
+// 6, 11.88 with 3, 12.04 with 2, 11.30-11.37 with 10, 12 or 16; Mixtral
+// prefill and the skewed layer also best or level at 8)
+constexpr int kPGroup = 8;
 // LDS: three activation buffers, then two weight buffers (160 KB)
 constexpr int kPWOff = 3 * kPSliceA;
 constexpr int kPLds = kPWOff + 2 * kPSliceW;
