@@ -71,8 +71,11 @@ def test_f32_layer_odd_shapes(T, d, f):
     _full_check(w)
 
 
+# (16, 4, 2100) and (64, 8, 4200): about 525 rows per expert, so the ping-pong kernel runs with
+# 16 and 64 experts of 2-3 row tiles each, full and partial, spread over the per-XCD tile ranges
 @pytest.mark.parametrize("E,k,T", [(1, 1, 20), (4, 1, 50), (2, 2, 9), (16, 4, 60), (64, 8, 50), (16, 4, 260),
-                                   (1, 1, 700), (2, 1, 333), (64, 8, 300), (32, 2, 5000)])
+                                   (1, 1, 700), (2, 1, 333), (64, 8, 300), (32, 2, 5000), (16, 4, 2100),
+                                   (64, 8, 4200)])
 def test_expert_and_k_variants(E, k, T):
     w = synthetic.make("decode", T=T, d=256, f=256, E=E, k=k, seed=E * 10 + k)
     _full_check(w)
