@@ -36,7 +36,7 @@ struct Plan {
   int gsplits = 1; // split-K factor of the streaming gate/up projection
   int bm = 256;    // tiled path: rows per workgroup tile
   int rsplits = 0; // split-K factor of the many-expert router GEMM (0: fused router)
-  int pp = 0;      // tiled path: the ping-pong kernel (bf16 weights, 256-row tiles)
+  int pp = 0;      // tiled path: the ping-pong kernel (bf16 weights; 1: 256-row tiles, 2: 320-row tiles)
   int64_t rows_cap = 0;
   size_t off_idx = 0, off_gate = 0, off_counts = 0, off_offsets = 0, off_perm = 0, off_pos = 0, off_pblk = 0;
   size_t off_tiles = 0;
@@ -109,7 +109,10 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
     // past 256 rows an expert's last 256-row tile is mostly empty yet streams
     // its whole weight tile; 320-row tiles (bf16) need fewer row tiles
     // (measured: 15% off the gate/up + down time at 287 rows per expert)
-    if (wdt == GROK_MOE_BF16 && r > 256) p.bm = 320;
+    if (wdt == GROK_MOE_BF16 && r > 256) {
+      p.bm = 320;
+      p.pp = 2;
+    }
     // from 512 rows per expert on, bf16 weights run the ping-pong kernel
     // (256-row tiles; measured: Grok-1 prefill layer 18.4 against 19.3-20.5
     // ms, Mixtral 8x22B prefill 9.4 against 9.9 ms, the skewed 2048-token
@@ -137,8 +140,8 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
     const int64_t exp_tiles =
         ((int64_t)E * ((T * k / E + p.bm - 1) / p.bm) + (int64_t)ns * ((T + p.bm - 1) / p.bm)) * dtiles;
     const int64_t last = exp_tiles % 256;
-    if (!p.pp && s == 1 && last > 0 && last <= 128 && (f / 2) % 64 == 0) s = 2;
-    if (p.pp && s == 1 && (f / 2) % 64 == 0) {
+    if (p.pp != 1 && s == 1 && last > 0 && last <= 128 && (f / 2) % 64 == 0) s = 2;
+    if (p.pp == 1 && s == 1 && (f / 2) % 64 == 0) {
       // ping-pong down tiles: an expert's last row tile is on average half
       // full, so about E (r / 256 + 1/2) row tiles run; two splits when that
       // leaves the last of fewer than 32 rounds at most three quarters full
@@ -333,9 +336,12 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
     GMOE_TRY(launch_stream_gateup(w8, p.mt_max, p.gsplits, (const bf16_bits*)A, rv, a->w_gate, a->w_up, a->scales, T,
                                   p.rows_cap, d, f, E, act, (bf16_bits*)H, (float*)(w + p.off_G), st));
   } else {
-    if (p.pp)
+    if (p.pp == 1)
       GMOE_TRY(launch_pp_gateup((const bf16_bits*)A, rv, (const bf16_bits*)a->w_gate, (const bf16_bits*)a->w_up, T,
                                 p.rows_cap, d, f, E, act, (bf16_bits*)H, st));
+    else if (p.pp == 2)
+      GMOE_TRY(launch_ppt_gateup((const bf16_bits*)A, rv, (const bf16_bits*)a->w_gate, (const bf16_bits*)a->w_up, T,
+                                 p.rows_cap, d, f, E, act, (bf16_bits*)H, st));
     else
       GMOE_TRY(launch_tiled_gateup(w8, p.bm, (const bf16_bits*)A, rv, a->w_gate, a->w_up, a->scales, T, p.rows_cap,
                                    d, f, E, act, (bf16_bits*)H, st));
@@ -348,9 +354,12 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
     GMOE_TRY(launch_stream_down(w8, p.mt_max, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d,
                                 f, E, Y, st));
   } else {
-    if (p.pp)
+    if (p.pp == 1)
       GMOE_TRY(launch_pp_down(p.splits, (const bf16_bits*)H, rv, (const bf16_bits*)a->w_down, p.rows_cap, d, f, E, Y,
                               st));
+    else if (p.pp == 2)
+      GMOE_TRY(launch_ppt_down(p.splits, (const bf16_bits*)H, rv, (const bf16_bits*)a->w_down, p.rows_cap, d, f, E, Y,
+                               st));
     else
       GMOE_TRY(launch_tiled_down(w8, p.bm, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d, f,
                                  E, Y, st));

@@ -72,10 +72,11 @@ def test_f32_layer_odd_shapes(T, d, f):
 
 
 # (16, 4, 2100) and (64, 8, 4200): about 525 rows per expert, so the ping-pong kernel runs with
-# 16 and 64 experts of 2-3 row tiles each, full and partial, spread over the per-XCD tile ranges
+# 16 and 64 experts of 2-3 row tiles each, full and partial, spread over the per-XCD tile ranges;
+# (16, 4, 1200) and (64, 8, 2400): about 300 rows per expert, the 320-row ping-pong tiles
 @pytest.mark.parametrize("E,k,T", [(1, 1, 20), (4, 1, 50), (2, 2, 9), (16, 4, 60), (64, 8, 50), (16, 4, 260),
                                    (1, 1, 700), (2, 1, 333), (64, 8, 300), (32, 2, 5000), (16, 4, 2100),
-                                   (64, 8, 4200)])
+                                   (64, 8, 4200), (16, 4, 1200), (64, 8, 2400)])
 def test_expert_and_k_variants(E, k, T):
     w = synthetic.make("decode", T=T, d=256, f=256, E=E, k=k, seed=E * 10 + k)
     _full_check(w)
@@ -302,9 +303,11 @@ def test_non_finite_tokens_stay_local(E, k, ns):
     (200, 320, 384, "bf16"),     # tiled, 128-row tiles; the down pass's 256-channel tile is ragged
     (700, 448, 1408, "bf16"),    # tiled, 256-row tiles
     (2100, 320, 384, "bf16"),    # ping-pong tiles (525 rows per expert)
+    (1200, 320, 384, "bf16"),    # 320-row ping-pong tiles (300 rows per expert); ragged down tile
     (8, 6208, 1408, "bf16"),     # d = 97 x 64, f = 11 x 128
     (8, 6208, 1408, "i8"),
     (2100, 6208, 1408, "bf16"),
+    (1200, 6208, 1408, "bf16"),  # 320-row ping-pong tiles, two down splits
     (2100, 384, 1408, "i8"),     # 8-bit at 525 rows per expert: tiled 256-row tiles, the down pass's last tile half past d
 ])
 def test_widths_multiple_of_64_and_128(T, d, f, w_dtype):
@@ -319,13 +322,14 @@ def test_widths_multiple_of_64_and_128(T, d, f, w_dtype):
     check_permutation(dbg["idx"], dbg, w.E)
     gates = np.take_along_axis(probs, dbg["idx"].astype(np.int64), 1)
     toks = None
-    if T * d * f > 2e9:   # sample: both edges of every 256-row tile of every expert, and 24 random tokens
+    if T * d * f > 2e9:   # sample: both edges of every 256- and 320-row tile of every expert, 24 random tokens
         offs, perm = dbg["offsets"], dbg["perm"]
         pick = set(np.random.default_rng(T).choice(T, 24, replace=False).tolist())
         for e in range(w.E):
             n = int(offs[e + 1] - offs[e])
-            for m0 in range(0, n, 256):
-                pick.update((int(perm[offs[e] + m0]), int(perm[offs[e] + min(n, m0 + 256) - 1])))
+            for bm in (256, 320):
+                for m0 in range(0, n, bm):
+                    pick.update((int(perm[offs[e] + m0]), int(perm[offs[e] + min(n, m0 + bm) - 1])))
         toks = sorted(pick)
     ref = oracle.forward_given_routing(w.x, w.w_gate, w.w_up, w.w_down, dbg["idx"], gates, scales=w.scales,
                                        tokens=toks)

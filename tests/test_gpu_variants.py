@@ -215,13 +215,16 @@ def test_fine_grained_fused_router_two_shared():
     _check(w, label="E=32 two shared")
 
 
-def test_fine_grained_pingpong_shared():
-    # 4,100 tokens over 32 routed experts (top-4) and one shared expert: about 621 rows per expert,
-    # so both projections run the ping-pong kernel, the SiLU epilogue included; the shared expert's
-    # 4,100 rows make 17 row tiles of one expert (two groups of 8 and a last group of one)
-    w = synthetic.make("dsv3_decode", T=4100, d=256, f=256, E=32, k=4, seed=11)
-    got, dbg, _ = _check(w, label="fine-grained ping-pong")
-    assert dbg["counts"][32] == 4100
+@pytest.mark.parametrize("T", [4100, 2000])
+def test_fine_grained_pingpong_shared(T):
+    # T tokens over 32 routed experts (top-4) and one shared expert, SiLU epilogue. 4,100 tokens:
+    # about 621 rows per expert, the 256-row ping-pong kernel (the shared expert's 4,100 rows make
+    # 17 row tiles of one expert: two groups of 8 and a last group of one). 2,000 tokens: about
+    # 303 rows per expert, the 320-row ping-pong kernel (the shared expert: 7 row tiles, the last
+    # of 80 rows)
+    w = synthetic.make("dsv3_decode", T=T, d=256, f=256, E=32, k=4, seed=11)
+    _, dbg, _ = _check(w, label="fine-grained ping-pong")
+    assert dbg["counts"][32] == T
 
 
 def test_fine_grained_int8_and_capacity():
