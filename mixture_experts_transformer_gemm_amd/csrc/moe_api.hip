@@ -36,7 +36,7 @@ struct Plan {
   int gsplits = 1; // split-K factor of the streaming gate/up projection
   int bm = 256;    // tiled path: rows per workgroup tile
   int rsplits = 0; // split-K factor of the many-expert router GEMM (0: fused router)
-  int pp = 0;      // tiled path: the ping-pong kernel (bf16 weights; 1: 256-row tiles, 2: 320-row tiles)
+  int pp = 0;      // tiled path: the ping-pong kernel (bf16 weights, 320-row tiles)
   int64_t rows_cap = 0;
   size_t off_idx = 0, off_gate = 0, off_counts = 0, off_offsets = 0, off_perm = 0, off_pos = 0, off_pblk = 0;
   size_t off_tiles = 0;
@@ -106,21 +106,15 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
     // on even when half of an expert's last tile is empty
     const int64_t r = p.rows_cap / Et;
     p.bm = r <= 32 ? 64 : (r <= 96 ? 128 : 256);
-    // past 256 rows an expert's last 256-row tile is mostly empty yet streams
-    // its whole weight tile; 320-row tiles (bf16) need fewer row tiles
-    // (measured: 15% off the gate/up + down time at 287 rows per expert)
-    if (wdt == GROK_MOE_BF16 && r > 256) {
+    // from about 200 rows per expert on, bf16 weights run the ping-pong
+    // kernel with 320-row tiles (measured against the tiled kernel with 256-
+    // or 320-row tiles and against a ping-pong kernel with 256-row tiles: the
+    // Grok-1 layer at 800 tokens 2.71 against 2.85 ms, at 1,200 tokens 3.09
+    // against 3.52, at 8,192 tokens 15.7 against 16.7, at 32,768 tokens 58.1
+    // against 66.6; the DeepSeek-V3-shaped prefill, about 287 rows per
+    // expert, 7.7 against 8.9 ms; level at 700 tokens, 0.17 ms slower at 600)
+    if (wdt == GROK_MOE_BF16 && r > 192) {
       p.bm = 320;
-      p.pp = 2;
-    }
-    // from 512 rows per expert on, bf16 weights run the ping-pong kernel
-    // (256-row tiles; measured: Grok-1 prefill layer 18.4 against 19.3-20.5
-    // ms, Mixtral 8x22B prefill 9.4 against 9.9 ms, the skewed 2048-token
-    // layer 5.4 against 6.0 ms); below, an expert's second 256-row tile is
-    // mostly empty (the 256-expert prefill, about 287 rows per expert: 9.6
-    // against 9.1 ms with 320-row tiles)
-    if (wdt == GROK_MOE_BF16 && r >= 512) {
-      p.bm = 256;
       p.pp = 1;
     }
     // 8-bit weights: 128-row tiles up to about 384 rows per expert (their
@@ -140,16 +134,9 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t ns
     const int64_t exp_tiles =
         ((int64_t)E * ((T * k / E + p.bm - 1) / p.bm) + (int64_t)ns * ((T + p.bm - 1) / p.bm)) * dtiles;
     const int64_t last = exp_tiles % 256;
-    if (p.pp != 1 && s == 1 && last > 0 && last <= 128 && (f / 2) % 64 == 0) s = 2;
-    if (p.pp == 1 && s == 1 && (f / 2) % 64 == 0) {
-      // ping-pong down tiles: an expert's last row tile is on average half
-      // full, so about E (r / 256 + 1/2) row tiles run; two splits when that
-      // leaves the last of fewer than 32 rounds at most three quarters full
-      const double rt = (double)E * ((double)T * k / E / 256.0 + 0.5) + (double)ns * ((double)T / 256.0 + 0.5);
-      const double rounds = rt * (double)dtiles / 256.0;
-      const double frac = rounds - floor(rounds);
-      if (rounds < 32.0 && frac > 0.0 && frac <= 0.75) s = 2;
-    }
+    // (the ping-pong kernel at 8,192 tokens, 1,344 tiles: 15.7 ms with two
+    // splits against 16.1 ms with one)
+    if (s == 1 && last > 0 && last <= 128 && (f / 2) % 64 == 0) s = 2;
     p.splits = s;
   }
   if (E > kFusedRouterE) {
@@ -336,12 +323,9 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
     GMOE_TRY(launch_stream_gateup(w8, p.mt_max, p.gsplits, (const bf16_bits*)A, rv, a->w_gate, a->w_up, a->scales, T,
                                   p.rows_cap, d, f, E, act, (bf16_bits*)H, (float*)(w + p.off_G), st));
   } else {
-    if (p.pp == 1)
+    if (p.pp)
       GMOE_TRY(launch_pp_gateup((const bf16_bits*)A, rv, (const bf16_bits*)a->w_gate, (const bf16_bits*)a->w_up, T,
                                 p.rows_cap, d, f, E, act, (bf16_bits*)H, st));
-    else if (p.pp == 2)
-      GMOE_TRY(launch_ppt_gateup((const bf16_bits*)A, rv, (const bf16_bits*)a->w_gate, (const bf16_bits*)a->w_up, T,
-                                 p.rows_cap, d, f, E, act, (bf16_bits*)H, st));
     else
       GMOE_TRY(launch_tiled_gateup(w8, p.bm, (const bf16_bits*)A, rv, a->w_gate, a->w_up, a->scales, T, p.rows_cap,
                                    d, f, E, act, (bf16_bits*)H, st));
@@ -354,12 +338,9 @@ int grok_moe_forward_ex(const grok_moe_args* a, void* ws, size_t ws_bytes, const
     GMOE_TRY(launch_stream_down(w8, p.mt_max, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d,
                                 f, E, Y, st));
   } else {
-    if (p.pp == 1)
+    if (p.pp)
       GMOE_TRY(launch_pp_down(p.splits, (const bf16_bits*)H, rv, (const bf16_bits*)a->w_down, p.rows_cap, d, f, E, Y,
                               st));
-    else if (p.pp == 2)
-      GMOE_TRY(launch_ppt_down(p.splits, (const bf16_bits*)H, rv, (const bf16_bits*)a->w_down, p.rows_cap, d, f, E, Y,
-                               st));
     else
       GMOE_TRY(launch_tiled_down(w8, p.bm, p.splits, (const bf16_bits*)H, rv, a->w_down, a->scales, p.rows_cap, d, f,
                                  E, Y, st));

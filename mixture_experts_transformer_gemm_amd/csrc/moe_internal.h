@@ -160,17 +160,12 @@ hipError_t launch_tiled_down(int w8, int bm, int splits, const bf16_bits* H, Rou
                              const float* scales, int64_t rows_cap, int d, int f, int E, float* Y,
                              hipStream_t stream);
 
-// Large-M path with bf16 weights: the ping-pong grouped GEMM (256-row tiles;
-// the tile table must be built for 256 rows).
+// Large-M path with bf16 weights: the ping-pong grouped GEMM (320-row tiles;
+// the tile table must be built for 320 rows).
 hipError_t launch_pp_gateup(const bf16_bits* x, RouteView rv, const bf16_bits* wg, const bf16_bits* wu, int64_t T,
                             int64_t rows_cap, int d, int f, int E, int act, bf16_bits* H, hipStream_t stream);
 hipError_t launch_pp_down(int splits, const bf16_bits* H, RouteView rv, const bf16_bits* wd, int64_t rows_cap, int d,
                           int f, int E, float* Y, hipStream_t stream);
-// The same with 320-row tiles (the tile table must be built for 320 rows).
-hipError_t launch_ppt_gateup(const bf16_bits* x, RouteView rv, const bf16_bits* wg, const bf16_bits* wu, int64_t T,
-                             int64_t rows_cap, int d, int f, int E, int act, bf16_bits* H, hipStream_t stream);
-hipError_t launch_ppt_down(int splits, const bf16_bits* H, RouteView rv, const bf16_bits* wd, int64_t rows_cap,
-                           int d, int f, int E, float* Y, hipStream_t stream);
 
 // fp32 path (plain FMA kernels, fp32 accumulation).
 hipError_t launch_f32_gateup(const float* x, RouteView rv, const float* wg, const float* wu, int64_t T,

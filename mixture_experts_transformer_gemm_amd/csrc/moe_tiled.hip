@@ -8,7 +8,7 @@
 // Down pass: Y = H Wd^T -> fp32.
 //
 // Workgroup tile: BM rows x 256 weight rows (BM = 64 or 128 with 4
-// wavefronts, 256 or 320 with 8). For the gate/up pass the 256 weight rows
+// wavefronts, 256 with 8). For the gate/up pass the 256 weight rows
 // are 128 gate channels and the same 128 up channels, so act(gate) * up is
 // formed in registers. With two wavefront rows, row subtile q (32 rows) goes
 // to wavefront row q mod 2, so a partly filled tile keeps both busy.
@@ -459,7 +459,7 @@ static unsigned tiled_blocks(int bm, int64_t rows_cap, int E, int nN) {
   return (unsigned)(((mt_ub * nN) + 7) / 8 * 8);
 }
 
-// Pipeline shape per tile height: 256- and 320-row tiles run 8 wavefronts
+// Pipeline shape per tile height: 256-row tiles run 8 wavefronts
 // (two per SIMD, so one's MFMAs cover the other's waits); as many LDS stages
 // as fit in 144 KB, at most 6, except for 8-bit weights, whose smaller
 // stages measured faster less deep: 2 stages for 256-row tiles (3.5% faster
@@ -507,9 +507,6 @@ static hipError_t tiled_dispatch(bool w8, int bm, hipStream_t st, const bf16_bit
       return tiled_launch<128, GATEUP>(w8, st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, act, out);
     case 256:
       return tiled_launch<256, GATEUP>(w8, st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, act, out);
-    case 320:  // bf16 weights only (the 8-bit instance spills and measured 9-15% slower than 256 rows)
-      if (w8) return hipErrorInvalidValue;
-      return launch_dma<320, GATEUP, false>(st, A, rv, w0, w1, scales, T, rows_cap, K, N, E, Ftot, splits, act, out);
   }
   return hipErrorInvalidValue;
 }

@@ -46,17 +46,16 @@ def test_workspace_bytes():
     # decode shape: idx/gate/perm/pos + H [16, f] bf16 + split-K Y partials
     ws = gm.grok_moe_workspace_bytes(8, 6144, 32768, 8, 2)
     assert ws >= 16 * 32768 * 2 + 16 * 6144 * 4
-    # prefill: H [16384, 32768] bf16 dominates; Y [2][16384, 6144] fp32 (about 8 x 8.5 row tiles of 256 x 24
-    # channel tiles = 1,632 down tiles leave the last of 256 workgroup rounds 38% full, so the reduction runs
+    # prefill: H [16384, 32768] bf16 dominates; Y [2][16384, 6144] fp32 (8 experts x 7 row tiles of 320 x 24
+    # channel tiles = 1,344 down tiles leave the last of 256 workgroup rounds 25% full, so the reduction runs
     # in two splits); u [8192, 6144] bf16 for the sandwich norms
     ws = gm.grok_moe_workspace_bytes(8192, 6144, 32768, 8, 2)
     assert 16384 * 32768 * 2 + 2 * 16384 * 6144 * 4 <= ws
     assert ws < 16384 * 32768 * 2 + 2 * 16384 * 6144 * 4 + 8192 * 6144 * 2 + (1 << 20)
-    # 16,384 tokens: about 8 x 16.5 row tiles of 256 x 24 channel tiles = 3,168 down tiles (12.4 rounds of 256
-    # CUs), two splits
+    # 16,384 tokens: 8 x 13 row tiles x 24 = 2,496 down tiles (9.75 rounds: the last 75% full), one split
     ws = gm.grok_moe_workspace_bytes(16384, 6144, 32768, 8, 2)
-    assert ws >= 32768 * 32768 * 2 + 2 * 32768 * 6144 * 4
-    # 32,768 tokens: about 6,240 down tiles (24.4 rounds), two splits
+    assert 32768 * 32768 * 2 + 32768 * 6144 * 4 <= ws < 32768 * 32768 * 2 + 2 * 32768 * 6144 * 4
+    # 32,768 tokens: 8 x 26 x 24 = 4,992 down tiles (19.5 rounds), two splits
     ws = gm.grok_moe_workspace_bytes(32768, 6144, 32768, 8, 2)
     assert ws >= 65536 * 32768 * 2 + 2 * 65536 * 6144 * 4
     assert gm.grok_moe_workspace_bytes(0, 6144, 32768, 8, 2) > 0
@@ -166,9 +165,11 @@ def test_workspace_bytes_ex_counts_shared_experts():
     (dict(T=8, d=6144, f=32768), 16),                                   # Grok-1 decode: streaming, 16-row chunks
     (dict(T=64, d=6144, f=32768), 64),
     (dict(T=256, d=6144, f=32768, w_dtype=gm.I8), 128),                # 8-bit streaming, 128-row chunks
-    (dict(T=8192, d=6144, f=32768), 256),                               # prefill: ping-pong 256-row tiles
-    (dict(T=8192, d=6144, f=32768, w_dtype=gm.I8), 256),
+    (dict(T=8192, d=6144, f=32768), 320),                               # prefill: ping-pong 320-row tiles
+    (dict(T=8192, d=6144, f=32768, w_dtype=gm.I8), 256),                # 8-bit: tiled 256-row tiles
     (dict(T=1100, d=256, f=512), 320),                                  # 275 rows per expert
+    (dict(T=800, d=256, f=512), 320),                                   # 200 rows per expert: ping-pong
+    (dict(T=700, d=256, f=512), 256),                                   # 175 rows per expert: tiled
     (dict(T=8192, d=7168, f=2048, E=256, k=8, n_shared=1), 320),        # 287 rows per expert
     (dict(T=300, d=256, f=512, w_dtype=gm.I8), 128),
     (dict(T=64, d=256, f=512, act_dtype=gm.F32, w_dtype=gm.F32), 0),   # fp32: no row tiles

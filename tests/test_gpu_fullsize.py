@@ -116,7 +116,7 @@ def test_skew_full():
 
 
 def test_int8_prefill_full():
-    # 8-bit weights at the prefill size: the 8-bit ping-pong kernel (256-row tiles, pairs of slices)
+    # 8-bit weights at the prefill size: the tiled 8-bit kernel (256-row tiles, int8 widened after the LDS read)
     dbg, counts = _run_and_check("int8", n_random=6, T=8192)
     assert counts.sum() == 2 * 8192
 

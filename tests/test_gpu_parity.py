@@ -72,8 +72,8 @@ def test_f32_layer_odd_shapes(T, d, f):
 
 
 # (16, 4, 2100) and (64, 8, 4200): about 525 rows per expert, so the ping-pong kernel runs with
-# 16 and 64 experts of 2-3 row tiles each, full and partial, spread over the per-XCD tile ranges;
-# (16, 4, 1200) and (64, 8, 2400): about 300 rows per expert, the 320-row ping-pong tiles
+# 16 and 64 experts of two 320-row tiles each, a full and a partial one, spread over the per-XCD
+# tile ranges; (16, 4, 1200) and (64, 8, 2400): about 300 rows per expert, mostly one partial tile
 @pytest.mark.parametrize("E,k,T", [(1, 1, 20), (4, 1, 50), (2, 2, 9), (16, 4, 60), (64, 8, 50), (16, 4, 260),
                                    (1, 1, 700), (2, 1, 333), (64, 8, 300), (32, 2, 5000), (16, 4, 2100),
                                    (64, 8, 4200), (16, 4, 1200), (64, 8, 2400)])
@@ -249,7 +249,7 @@ def test_permutation_many_blocks(E, k, cf):
                                               ("i8", 64, [1, 17, 33, 49, 28, 0, 0, 0])])
 def test_tile_boundaries_and_empty_experts(w_dtype, T, sizes):
     # 1,100 tokens at top-2 average 275 rows per expert, so bf16 weights run 320-row tiles (8-bit: 128-row);
-    # 2,100 tokens average 525, which runs the 256-row ping-pong tiles (8-bit: tiled, 256-row). Segments of 0, 1, 255 .. 257,
+    # 2,100 tokens average 525, the same tiles (8-bit: tiled, 256-row). Segments of 0, 1, 255 .. 257,
     # 319 .. 321, 512, 513, 640, 1024 and 1025 rows put tile edges on both sides of every boundary, and
     # empty first and last experts must be skipped by the tile table. With 8-bit weights and 65 .. 256
     # (up to 64) tokens the streaming kernel runs 128-row (64-row) chunks, and segments of 1, 17, .., 113
@@ -302,7 +302,7 @@ def test_non_finite_tokens_stay_local(E, k, ns):
     (200, 320, 384, "i8"),
     (200, 320, 384, "bf16"),     # tiled, 128-row tiles; the down pass's 256-channel tile is ragged
     (700, 448, 1408, "bf16"),    # tiled, 256-row tiles
-    (2100, 320, 384, "bf16"),    # ping-pong tiles (525 rows per expert)
+    (2100, 320, 384, "bf16"),    # ping-pong tiles (525 rows per expert: a full and a partial tile)
     (1200, 320, 384, "bf16"),    # 320-row ping-pong tiles (300 rows per expert); ragged down tile
     (8, 6208, 1408, "bf16"),     # d = 97 x 64, f = 11 x 128
     (8, 6208, 1408, "i8"),

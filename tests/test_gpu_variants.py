@@ -217,11 +217,11 @@ def test_fine_grained_fused_router_two_shared():
 
 @pytest.mark.parametrize("T", [4100, 2000])
 def test_fine_grained_pingpong_shared(T):
-    # T tokens over 32 routed experts (top-4) and one shared expert, SiLU epilogue. 4,100 tokens:
-    # about 621 rows per expert, the 256-row ping-pong kernel (the shared expert's 4,100 rows make
-    # 17 row tiles of one expert: two groups of 8 and a last group of one). 2,000 tokens: about
-    # 303 rows per expert, the 320-row ping-pong kernel (the shared expert: 7 row tiles, the last
-    # of 80 rows)
+    # T tokens over 32 routed experts (top-4) and one shared expert, SiLU epilogue, on the
+    # ping-pong kernel. 4,100 tokens: about 621 rows per expert, and the shared expert's 4,100
+    # rows make 13 row tiles of one expert (a group of 8 and a last group of 5, the last tile
+    # 260 rows). 2,000 tokens: about 303 rows per expert (the shared expert: 7 row tiles, the
+    # last of 80 rows)
     w = synthetic.make("dsv3_decode", T=T, d=256, f=256, E=32, k=4, seed=11)
     _, dbg, _ = _check(w, label="fine-grained ping-pong")
     assert dbg["counts"][32] == T
