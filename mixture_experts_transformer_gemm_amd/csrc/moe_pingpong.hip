@@ -1,16 +1,17 @@
-// Tall ping-pong grouped GEMM of the MoE layer for gfx950 (MI355X): the
-// gate/up and down projections with bf16 weights when experts hold a little
-// more than 256 rows, as in the fine-grained layer's prefill (book ch. 10,
-// section 10.1 table: 256 routed experts, top-8, so 8192 tokens give about
-// 256 rows per expert, and the shared expert takes every token).
+// Ping-pong grouped GEMM of the MoE layer for gfx950 (MI355X): the gate/up
+// and down projections with bf16 weights once experts hold about 200 rows or
+// more (the Grok-1 and Mixtral prefill, the skewed layer, and the
+// fine-grained layer's prefill, where 8192 tokens give about 256 rows per
+// expert; book ch. 10, section 10.1 table). Each expert is one segment of a
+// grouped GEMM over the expert-contiguous permutation (book ch. 11, section
+// 11.3.1: sparse reorder, then grouped GEMM): the gate/up pass forms H =
+// act(X Wg^T) * (X Wu^T) in bf16, the down pass Y = H Wd^T as fp32 partial
+// sums.
 //
-// Same computation as the 256-row ping-pong kernel (one segment of a grouped
-// GEMM per expert over the expert-contiguous permutation; gate/up pass H =
-// act(X Wg^T) * (X Wu^T) in bf16, down pass Y = H Wd^T in fp32 partial sums),
-// with 320-row tiles: an expert of 257-320 rows is one tile instead of a full
-// and a nearly empty 256-row tile, each of which streams the whole weight tile.
-//
-// Workgroup tile: 320 rows x 256 weight rows, 8 wavefronts, two per SIMD.
+// Workgroup tile: 320 rows x 256 weight rows, 8 wavefronts, two per SIMD
+// (wavefronts w and w + 4 share a SIMD on gfx950). 320-row tiles leave an
+// expert of 257-320 rows one tile instead of a full and a nearly empty
+// 256-row tile, each of which would stream the whole weight tile.
 // Products use v_mfma_f32_16x16x32_bf16 (20 row tiles of 16 split evenly over
 // the 4 SIMDs; 320 rows are 10 tiles of 32, which 4 SIMDs cannot share
 // evenly): lane l supplies row (l mod 16) and reduction values 8 (l / 16) ..
@@ -20,21 +21,23 @@
 // (rows 16 (s + 4 j) .. + 15, j = 0..4) in 160 fp32 accumulator registers.
 //
 // The reduction runs in slices of 64 values; every load instruction
-// (global_load_lds_dwordx4) fills one 1 KB LDS block of 8 rows x 128 bytes.
+// (global_load_lds_dwordx4) fills one 1 KB LDS block of 8 rows x 128 bytes,
+// so the 8 lanes of a row fetch one whole 128-byte line.
 // LDS holds two activation slices (40 KB each) and two weight slices (32 KB
-// each), 144 KB. The two groups take turns between barriers as in the 256-row
-// kernel: one group issues MFMAs on fragments already in registers while the
-// other reads the next fragments from LDS and issues loads. A slice is read
-// in four phases (half 0 by group 0, half 0 by group 1, half 1 by group 0,
-// half 1 by group 1). Activations of slice sl + 1 are loaded in the first two
-// phases of slice sl, into the buffer of slice sl - 1 (both groups read every
-// activation row, so that buffer is free only once slice sl - 1 is done);
-// each group loads its own weight rows of slice sl + 2 right after its last
-// read of slice sl (the groups read disjoint weight rows). Before the barrier
-// that ends a slice, every wavefront waits for its loads of the next slice.
-// Weights, which at this shape stream from HBM once per tile, thus get about
-// six phases to arrive; activations, shared by all channel tiles of an expert
-// and mostly served by L2, about three.
+// each), 144 KB. The two wavefront groups take turns between workgroup
+// barriers: one group issues MFMAs on fragments already in registers while
+// the other reads the next fragments from LDS and issues loads, so each
+// SIMD's matrix core is fed by one wavefront while its partner waits on
+// memory. A slice is read in four phases (half 0 by group 0, half 0 by group
+// 1, half 1 by group 0, half 1 by group 1). Activations of slice sl + 1 are
+// loaded in the first two phases of slice sl, into the buffer of slice sl - 1
+// (both groups read every activation row, so that buffer is free only once
+// slice sl - 1 is done); each group loads its own weight rows of slice sl + 2
+// right after its last read of slice sl (the groups read disjoint weight
+// rows). Before the barrier that ends a slice, every wavefront waits for its
+// loads of the next slice. Weights get about six phases to arrive;
+// activations, shared by all channel tiles of an expert and mostly served by
+// L2, about three.
 #include "moe_device.h"
 
 #include <type_traits>
@@ -51,7 +54,7 @@ constexpr int kPSliceA = kPM * kPRow;       // activation half of a slice: 40 KB
 constexpr int kPSliceW = kPN * kPRow;       // weight half: 32 KB
 constexpr int kPWOff = 2 * kPSliceA;        // two activation buffers, then two weight buffers
 constexpr int kPLds = kPWOff + 2 * kPSliceW;  // 144 KB
-constexpr int kPGroup = 8;                  // row tiles per tile group (as the 256-row kernel)
+constexpr int kPGroup = 8;                  // row tiles per tile group
 constexpr int kPABlk = kPM / 8 / 8;         // activation blocks per wavefront and slice: 5
 
 struct PTile {
