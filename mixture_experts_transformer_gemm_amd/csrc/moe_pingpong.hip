@@ -54,7 +54,7 @@ constexpr int kPSliceA = kPM * kPRow;       // activation half of a slice: 40 KB
 constexpr int kPSliceW = kPN * kPRow;       // weight half: 32 KB
 constexpr int kPWOff = 2 * kPSliceA;        // two activation buffers, then two weight buffers
 constexpr int kPLds = kPWOff + 2 * kPSliceW;  // 144 KB
-constexpr int kPGroup = 8;                  // row tiles per tile group
+constexpr int kPGroup = 4;                  // row tiles per tile group
 constexpr int kPABlk = kPM / 8 / 8;         // activation blocks per wavefront and slice: 5
 
 struct PTile {
@@ -67,6 +67,14 @@ struct PTile {
 // numbering is split into 8 contiguous ranges, one per XCD (workgroup i runs
 // on XCD i mod 8). Output channels per tile: 128 (gate/up: 128 gate + the
 // same 128 up weight rows) or 256 (down).
+//
+// An XCD runs 32 tiles at once (one per CU), so a group of 4 row tiles moves
+// through its channel tiles 8 at a time, each round 4 activation slices and
+// 8 weight slices shared through the XCD's L2. A group that holds all 7 row
+// tiles of a Grok-1 prefill expert runs 7 x 4.6 tiles per round instead:
+// rounds straddle channel tiles, whose weights are then fetched again a
+// tile's time later (FETCH_SIZE of the gate/up launch 63 GB against 32 GB
+// with groups of 4, and 2-3% slower).
 template <bool GATEUP>
 __device__ __forceinline__ bool pp_select(const RouteView& rv, int E, int N, PTile& t) {
   constexpr int kCh = GATEUP ? kPN / 2 : kPN;
