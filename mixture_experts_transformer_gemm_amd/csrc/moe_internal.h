@@ -32,40 +32,37 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// Round to nearest even (NaN inputs are outside the layer's contract).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Two floats -> packed pair of bf16 (lo in the low half).
+// Two floats -> packed pair of bf16 (lo in the low half), rounded to nearest
+// even: one v_cvt_pk_bf16_f32 on gfx950 (what the compiler emits for the
+// __bf16 conversions), where a software rounding takes five instructions
+// per pair.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-// Exact-erf GELU: z * Phi(z), Phi(z) = erfc(-z / sqrt 2) / 2. Phi(-|z|) = erfc(u) / 2 with
-// u = |z| / sqrt 2 comes from the Chebyshev fit of Numerical Recipes (Press et al., 2nd ed., section
-// 6.2, erfcc): erfc(u) = t exp(P(t) - u^2), t = 2 / (2 + u), P of degree 9, fractional error below
-// 1.2e-7 for every u >= 0; Phi(|z|) = 1 - Phi(-|z|). Branch-free: one v_rcp_f32, ten FMAs and one
-// v_exp_f32 (about 1 ulp each), where the device library's erff costs about 70 instructions with
-// divergent range branches. Evaluated in fp32 against the fp64 GELU: relative error below 3e-6 for
-// |z| <= 4, below 2e-5 everywhere (the far negative tail, where the rounding of the exponent grows),
-// absolute error below 4e-7.
+// Exact-erf GELU: z * Phi(z) (Phi the standard normal CDF, Phi(z) = erfc(-z / sqrt 2) / 2), with the
+// tail Phi(-|z|) = 1 - Phi(|z|) from the rational-times-density approximation of Abramowitz and
+// Stegun, 26.2.17 (after Hastings): Phi(-x) = phi(x) t (b1 + t (b2 + t (b3 + t (b4 + t b5)))),
+// t = 1 / (1 + 0.2316419 x), x >= 0, absolute error below 7.5e-8; Phi(|z|) = 1 - Phi(-|z|). The
+// density phi(x) = e^(-x^2 / 2) / sqrt(2 pi) is one v_exp_f32 of an FMA (1 / sqrt(2 pi) folded into
+// the exponent). Branch-free: one v_rcp_f32, four FMAs for the polynomial, one v_exp_f32 (about 1 ulp
+// each), where the device library's erff costs about 70 instructions with divergent range branches.
+// Evaluated in fp32 against the fp64 GELU: absolute error below 3e-7 max(1, |z|), relative below
+// 1e-6 for z >= 0; the far negative tail, where GELU is below 1e-7 in magnitude, is exact only
+// to that absolute bound. H is rounded to bf16 after it, a relative step of 2^-9.
 __device__ __forceinline__ float gelu_erf(float z) {
-  const float u = fabsf(z) * 0.70710678118654752f;
-  const float t = 2.0f * __builtin_amdgcn_rcpf(2.0f + u);
-  float p = 0.17087277f;
-  p = fmaf(p, t, -0.82215223f);
-  p = fmaf(p, t, 1.48851587f);
-  p = fmaf(p, t, -1.13520398f);
-  p = fmaf(p, t, 0.27886807f);
-  p = fmaf(p, t, -0.18628806f);
-  p = fmaf(p, t, 0.09678418f);
-  p = fmaf(p, t, 0.37409196f);
-  p = fmaf(p, t, 1.00002368f);
-  p = fmaf(p, t, -1.26551223f);
-  const float q = 0.5f * t * __builtin_amdgcn_exp2f((p - u * u) * 1.44269504088896341f);  // Phi(-|z|)
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.2316419f, fabsf(z), 1.0f));
+  float p = 1.330274429f;
+  p = fmaf(p, t, -1.821255978f);
+  p = fmaf(p, t, 1.781477937f);
+  p = fmaf(p, t, -0.356563782f);
+  p = fmaf(p, t, 0.319381530f);
+  // phi(z) = 2^(-z^2 log2(e) / 2 - log2(sqrt(2 pi)))
+  const float phi = __builtin_amdgcn_exp2f(fmaf(z * z, -0.72134752044448170f, -1.32574806473615930f));
+  const float q = t * p * phi;  // Phi(-|z|)
   return z * (z >= 0.0f ? 1.0f - q : q);
 }
 
