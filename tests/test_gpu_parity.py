@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synthetic
-from gpu_util import TOL, check_permutation, check_routing, dev_workload, normwise_err, run_layer
+from gpu_util import TOL, check_permutation, check_routing, dev_workload, elementwise_err, normwise_err, run_layer
 
 torch = pytest.importorskip("torch")
 import mixture_experts_transformer_gemm_amd as gm  # noqa: E402
@@ -96,6 +96,29 @@ def test_routing_override_imbalanced(T):
     assert list(dbg["counts"]) == [0, 0, 0, T, 0, 0, T, 0]
     ref = oracle.forward_given_routing(w.x, w.w_gate, w.w_up, w.w_down, idx, gate.astype(np.float64))
     assert normwise_err(got, ref) <= TOL["bf16"]
+
+
+# Expert segments of 5, 6, 9 and 10 row tiles of 320 rows: the ping-pong kernel walks an expert's
+# row tiles in groups of 4, then the remainder (4 + 1, 4 + 2, 4 + 4 + 1, 4 + 4 + 2), here next to an
+# empty expert, a one-row expert, one exact tile and one tile plus a row, through a caller routing
+# with k = 1 and per-token gates.
+def test_pingpong_tile_groups_with_remainders():
+    counts = [1500, 1800, 0, 2600, 1, 3000, 320, 321]
+    T = sum(counts)
+    w = synthetic.make("decode", T=T, d=256, f=512, k=1, seed=11)
+    dev = dev_workload(w, torch)
+    assert gm.grok_moe_tile_rows(dev["x"], dev["router_w"], dev["w_gate"], dev["w_up"], dev["w_down"], k=1) == 320
+    rng = np.random.default_rng(3)
+    idx = np.repeat(np.arange(w.E, dtype=np.int32), counts)[rng.permutation(T)][:, None]
+    gate = rng.uniform(0.25, 1.0, (T, 1)).astype(np.float32)
+    got, dbg = run_layer(w, torch, dev=dev, route_idx=idx, route_gate=gate)
+    check_permutation(idx, dbg, w.E)
+    assert list(dbg["counts"]) == counts
+    ref = oracle.forward_given_routing(w.x, w.w_gate, w.w_up, w.w_down, idx, gate.astype(np.float64))
+    err, eerr = normwise_err(got, ref), elementwise_err(got, ref)
+    print(f"tile-group remainders: normwise {err:.3e}, elementwise {eerr:.3e}")
+    assert err <= TOL["bf16"]
+    assert np.all(np.isfinite(got))
 
 
 def test_routing_override_single_expert_k1():
