@@ -170,6 +170,8 @@ def test_workspace_bytes_ex_counts_shared_experts():
     (dict(T=1100, d=256, f=512), 320),                                  # 275 rows per expert
     (dict(T=800, d=256, f=512), 320),                                   # 200 rows per expert: ping-pong
     (dict(T=700, d=256, f=512), 256),                                   # 175 rows per expert: tiled
+    (dict(T=772, d=256, f=512), 320),                                   # 193 rows per expert: ping-pong
+    (dict(T=768, d=256, f=512), 256),                                   # 192 rows per expert: tiled
     (dict(T=8192, d=7168, f=2048, E=256, k=8, n_shared=1), 320),        # 287 rows per expert
     (dict(T=300, d=256, f=512, w_dtype=gm.I8), 128),
     (dict(T=64, d=256, f=512, act_dtype=gm.F32, w_dtype=gm.F32), 0),   # fp32: no row tiles
